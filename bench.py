@@ -1,0 +1,189 @@
+"""Benchmark of the MSA prefill forward + backward on one MI355X.
+
+One step = the whole path on one batch: forward (k2q CSR, plan, K/V alignment,
+forward kernel) then backward (delta preprocessing, task tables, backward: pool
+zeroing, main KV-parallel kernel, finalize).  Inputs are resident in HBM before the
+timed region.  Prints one JSON line.
+
+Effective FLOPs count only selected blocks: every member block of an (index head,
+query) counts its 128 keys for each of the 16 query heads, 4*128 flops per (row, key)
+forward and 10*128 backward.  Timing protocol of the pages' operator benchmark:
+warmup steps, then a timed loop; per-phase medians come from HIP events.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+WORKLOAD_NAMES = {
+    0: "single 512-token document, all causal blocks (dense causal GQA)",
+    1: "one packed 16384-token row of 512..6000-token documents, uniform top-16",
+    2: "single 16384-token document, diagonal + sink + 14 uniform blocks (top-16)",
+    3: "single 65536-token document, diagonal + 3 local + 12 distance-decaying blocks",
+    4: "4 packed 16384-token rows of short geometric documents, Zipf-skewed selection",
+}
+
+
+def member_slots(q2k, cu):
+    """Count of member slots: ids in [0, blk(t)], first listing in the row."""
+    T = int(cu[-1])
+    t = np.arange(T)
+    doc = np.searchsorted(cu, t, side="right") - 1
+    blk = (t - cu[doc]) // 128
+    ok = (q2k >= 0) & (q2k <= blk[None, :, None])
+    first = np.ones_like(ok)
+    for j in range(1, q2k.shape[2]):
+        first[:, :, j] = ~np.any(q2k[:, :, :j] == q2k[:, :, j:j + 1], axis=2)
+    return int((ok & first).sum())
+
+
+def cpu_baseline(cfg, budget_tokens):
+    """The fp64 oracle on a bounded sample: the first `budget_tokens` queries of the
+    workload's first document with their own selections.  A prefix of a causal
+    document attends only to keys inside the prefix, so it is an exact sub-workload."""
+    import workloads as WL
+    from oracle import oracle as OR
+    cu, q2k = WL.make_structure(cfg)
+    Tp = min(budget_tokens, int(cu[1]))
+    cup = np.array([0, Tp], dtype=np.int32)
+    qp = np.ascontiguousarray(q2k[:, :Tp])
+    tens = WL.make_tensors(int(cu[-1]), 1000 + cfg)
+    Q, K, V, dO = (tens[k][:Tp].float().numpy().astype(np.float64) for k in ("Q", "K", "V", "dO"))
+    scale = 1.0 / math.sqrt(128.0)
+    OR.build(force=False)
+    t0 = time.perf_counter()
+    OR.forward(Q, K, V, qp, cup, scale)
+    t1 = time.perf_counter()
+    OR.backward(Q, K, V, dO, qp, cup, scale)
+    t2 = time.perf_counter()
+    fwd, bwd, _ = OR.effective_flops(qp, cup)
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {"value": round((fwd + bwd) / (t2 - t0) / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "first %d queries of the first document of workload %d (exact causal "
+                      "sub-workload), fp64 forward %.1f s + backward %.1f s" % (Tp, cfg, t1 - t0, t2 - t1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--dq-mode", choices=["fp32", "bf16x2"], default="bf16x2")
+    ap.add_argument("--grid", type=int, default=0)
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the operator runs on a single MI355X and this "
+              "build has no multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_q2k_amd as M
+    import workloads as WL
+    if not os.path.exists(M._LIB_PATH):
+        from block_sparse_attention_q2k_amd import build
+        build.build()
+    M.lib()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    cu, q2k = WL.make_structure(args.config)
+    T = int(cu[-1])
+    tens = WL.make_tensors(T, 1000 + args.config, device=dev)
+    Q, K, V, dO = tens["Q"], tens["K"], tens["V"], tens["dO"]
+    q2k_d = torch.from_numpy(q2k).to(dev)
+    scale = 1.0 / math.sqrt(128.0)
+    mode = M.DQ_ACCUM_FP32 if args.dq_mode == "fp32" else M.DQ_ACCUM_BF16X2
+    m = M.MSA(cu, grid=args.grid or None, dq_mode=mode, device=dev)
+    O = torch.empty_like(Q)
+    LSE = torch.empty((T, 64), dtype=torch.float32, device=dev)
+    dQ = torch.empty_like(Q)
+    dK = torch.empty_like(K)
+    dV = torch.empty_like(V)
+
+    slots = member_slots(q2k, cu)
+    fwd_flops = 4.0 * 128 * 128 * 16 * slots
+    bwd_flops = 2.5 * fwd_flops
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        m.forward(Q, K, V, q2k_d, scale, O=O, LSE=LSE)
+        if ev:
+            ev[1].record()
+        m.backward(Q, dO, O, LSE, scale, dQ=dQ, dK=dK, dV=dV)
+        if ev:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        M.msa_set_backward_timing_events(kev[k][0], kev[k][1])
+        step(evs[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    M.msa_set_backward_timing_events(None, None)
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    main_ms = [e[0].elapsed_time(e[1]) for e in kev]
+    ms_step = elapsed * 1e3 / args.steps
+    total_flops = fwd_flops + bwd_flops
+    value = total_flops / (ms_step * 1e-3) / 1e12
+    main_avg = float(np.mean(main_ms))
+    achieved = bwd_flops / (main_avg * 1e-3) / 1e12
+    status = int(m.status[0].item())
+
+    out = {
+        "metric": "MSA fwd+bwd effective TFLOP/s + ms/layer at 16k packed tokens, 1 MI355X",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; see workloads.py)",
+        "config": {"workload": "config %d: %s" % (args.config, WORKLOAD_NAMES[args.config]),
+                   "tokens": T, "documents": len(cu) - 1, "q_heads": 64, "kv_heads": 4,
+                   "index_heads": 4, "head_dim": 128, "block": 128, "topk": 16,
+                   "dq_accum": args.dq_mode, "grid": m.grid, "member_slots": slots},
+        "fwd_ms_median": round(float(np.median(fwd_ms)), 4),
+        "bwd_ms_median": round(float(np.median(bwd_ms)), 4),
+        "fwd_tflops": round(fwd_flops / (np.median(fwd_ms) * 1e-3) / 1e12, 3),
+        "bwd_tflops": round(bwd_flops / (np.median(bwd_ms) * 1e-3) / 1e12, 3),
+        "fwd_frac_mfma_peak": round(fwd_flops / (np.median(fwd_ms) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "bwd_frac_mfma_peak": round(bwd_flops / (np.median(bwd_ms) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "q2k_status": status,
+        "roofline": {"kernel": "bwd_kernel (main KV-parallel backward)", "bound": "mfma",
+                     "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "avg_launch_ms": round(main_avg, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

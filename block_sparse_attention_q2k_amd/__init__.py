@@ -1,0 +1,283 @@
+"""Python binding of libmsa, the MI355X (gfx950) MSA prefill forward/backward library.
+
+Argument marshalling only: every step of the operator runs in the HIP kernels behind
+the C ABI declared in ``include/msa.h``.  PyTorch provides device memory and streams.
+The functions below carry the C names; ``MSA`` bundles one layout's buffers and runs
+the call sequence (forward: CSR, plan, K/V alignment, forward; backward: preprocess,
+task tables, backward).  If the library is not built, loading fails loudly -- there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB as _LIB_PATH
+
+NUM_Q_HEADS, NUM_KV_HEADS, NUM_INDEX_HEADS, HEAD_DIM, BLOCK, TOPK = 64, 4, 4, 128, 128, 16
+TILE_QUERIES, FWD_GROUP = 8, 16
+DQ_ACCUM_FP32, DQ_ACCUM_BF16X2 = 0, 1
+Q2K_OUT_OF_RANGE, Q2K_DUPLICATE = 1, 2
+PLAN_HEADER_WORDS, TASKS_HEADER_WORDS = 16, 64
+
+
+class MSAError(RuntimeError):
+    def __init__(self, fn, rc, text):
+        super().__init__("%s failed: %d (%s)" % (fn, rc, text))
+        self.rc = rc
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("num_docs", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+                ("num_ws_tokens", ctypes.c_int32), ("cu_seqlens", ctypes.c_void_p),
+                ("cu_ws", ctypes.c_void_p)]
+
+
+_lib = None
+EXPORTS = ["msa_layout_host", "msa_csr_scratch_bytes", "msa_csr_cols_capacity", "msa_plan_bytes",
+           "msa_tasks_bytes", "msa_bwd_scratch_bytes", "msa_default_grid", "msa_align_kv",
+           "msa_build_k2q_csr", "msa_plan", "msa_forward", "msa_backward_preprocess",
+           "msa_tasks_meta_offset", "msa_build_tasks", "msa_backward", "msa_status_string",
+           "msa_set_backward_timing_events"]
+
+
+def lib():
+    """Load libmsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libmsa.so is not built (%s); run block_sparse_attention_q2k_amd.build"
+                               % _LIB_PATH)
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I, Z, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+        LP = ctypes.POINTER(_Layout)
+        sig = {
+            "msa_layout_host": (I, [P, I, P, P]),
+            "msa_csr_scratch_bytes": (Z, [LP]),
+            "msa_csr_cols_capacity": (Z, [LP]),
+            "msa_plan_bytes": (Z, [LP]),
+            "msa_tasks_bytes": (Z, [LP, I]),
+            "msa_bwd_scratch_bytes": (Z, [LP, I]),
+            "msa_default_grid": (I, []),
+            "msa_align_kv": (I, [P, P, LP, P, P, P]),
+            "msa_build_k2q_csr": (I, [P, LP, P, P, P, P, Z, P]),
+            "msa_plan": (I, [LP, P, P, Z, P]),
+            "msa_forward": (I, [P, P, P, P, LP, P, F, P, P, P]),
+            "msa_backward_preprocess": (I, [P, P, I, P, P]),
+            "msa_tasks_meta_offset": (Z, [I]),
+            "msa_build_tasks": (I, [LP, P, P, I, P, Z, P]),
+            "msa_backward": (I, [P, P, P, P, P, P, P, I, LP, F, I, P, P, P, P, Z, P]),
+            "msa_status_string": (ctypes.c_char_p, [I]),
+            "msa_set_backward_timing_events": (None, [P, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise MSAError(fn, rc, lib().msa_status_string(rc).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def msa_layout_host(cu_seqlens):
+    """(cu_ws int32 numpy [N+1], W) for host document offsets; raises on bad offsets."""
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    cu_ws = np.zeros_like(cu)
+    W = ctypes.c_int32(0)
+    _check("msa_layout_host", lib().msa_layout_host(cu.ctypes.data_as(ctypes.c_void_p), len(cu) - 1,
+                                                   cu_ws.ctypes.data_as(ctypes.c_void_p),
+                                                   ctypes.byref(W)))
+    return cu_ws, int(W.value)
+
+
+class Layout:
+    """Packed-document layout: host offsets plus their device copies."""
+
+    def __init__(self, cu_seqlens, device="cuda"):
+        import torch
+        self.cu_host = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        self.cu_ws_host, self.W = msa_layout_host(self.cu_host)
+        self.num_docs = len(self.cu_host) - 1
+        self.T = int(self.cu_host[-1])
+        self.NB = self.W // BLOCK
+        self.cu = torch.from_numpy(self.cu_host).to(device)
+        self.cu_ws = torch.from_numpy(self.cu_ws_host).to(device)
+        self.c = _Layout(self.num_docs, self.T, self.W, self.cu.data_ptr(), self.cu_ws.data_ptr())
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def msa_csr_scratch_bytes(layout):
+    return lib().msa_csr_scratch_bytes(layout.ref())
+
+
+def msa_csr_cols_capacity(layout):
+    return lib().msa_csr_cols_capacity(layout.ref())
+
+
+def msa_plan_bytes(layout):
+    return lib().msa_plan_bytes(layout.ref())
+
+
+def msa_tasks_bytes(layout, grid):
+    return lib().msa_tasks_bytes(layout.ref(), grid)
+
+
+def msa_bwd_scratch_bytes(layout, mode):
+    return lib().msa_bwd_scratch_bytes(layout.ref(), mode)
+
+
+def msa_default_grid():
+    return lib().msa_default_grid()
+
+
+def msa_tasks_meta_offset(grid):
+    return lib().msa_tasks_meta_offset(grid)
+
+
+def msa_align_kv(K, V, layout, Kw, Vw, stream=None):
+    _check("msa_align_kv", lib().msa_align_kv(_ptr(K), _ptr(V), layout.ref(), _ptr(Kw), _ptr(Vw),
+                                              _stream(stream)))
+
+
+def msa_build_k2q_csr(q2k, layout, row_ptr, cols, status, scratch, stream=None):
+    _check("msa_build_k2q_csr", lib().msa_build_k2q_csr(
+        _ptr(q2k), layout.ref(), _ptr(row_ptr), _ptr(cols), _ptr(status), _ptr(scratch),
+        scratch.numel() * scratch.element_size(), _stream(stream)))
+
+
+def msa_plan(layout, q2k, plan, stream=None):
+    _check("msa_plan", lib().msa_plan(layout.ref(), _ptr(q2k), _ptr(plan),
+                                      plan.numel() * plan.element_size(), _stream(stream)))
+
+
+def msa_forward(Q, Kw, Vw, q2k, layout, plan, scale, O, LSE, stream=None):
+    _check("msa_forward", lib().msa_forward(_ptr(Q), _ptr(Kw), _ptr(Vw), _ptr(q2k), layout.ref(),
+                                            _ptr(plan), float(scale), _ptr(O), _ptr(LSE),
+                                            _stream(stream)))
+
+
+def msa_backward_preprocess(O, dO, num_tokens, delta, stream=None):
+    _check("msa_backward_preprocess", lib().msa_backward_preprocess(
+        _ptr(O), _ptr(dO), int(num_tokens), _ptr(delta), _stream(stream)))
+
+
+def msa_build_tasks(layout, row_ptr, cols, grid, tasks, stream=None):
+    _check("msa_build_tasks", lib().msa_build_tasks(layout.ref(), _ptr(row_ptr), _ptr(cols), int(grid),
+                                                    _ptr(tasks), tasks.numel() * tasks.element_size(),
+                                                    _stream(stream)))
+
+
+def msa_backward(Q, Kw, Vw, dO, LSE, delta, tasks, grid, layout, scale, mode, dQ, dK, dV, scratch,
+                 stream=None):
+    _check("msa_backward", lib().msa_backward(
+        _ptr(Q), _ptr(Kw), _ptr(Vw), _ptr(dO), _ptr(LSE), _ptr(delta), _ptr(tasks), int(grid),
+        layout.ref(), float(scale), int(mode), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(scratch),
+        scratch.numel() * scratch.element_size(), _stream(stream)))
+
+
+def msa_set_backward_timing_events(start, stop):
+    """start/stop: torch.cuda.Event objects (or None, None to turn the hook off)."""
+    lib().msa_set_backward_timing_events(
+        None if start is None else ctypes.c_void_p(start.cuda_event),
+        None if stop is None else ctypes.c_void_p(stop.cuda_event))
+
+
+def _bytes(n, device):
+    import torch
+    return torch.empty(max(16, (int(n) + 15) // 16 * 16), dtype=torch.uint8, device=device)
+
+
+class MSA:
+    """Buffers of one layout plus the forward and backward call sequences."""
+
+    def __init__(self, cu_seqlens, grid=None, dq_mode=DQ_ACCUM_FP32, device="cuda"):
+        import torch
+        self.layout = L = Layout(cu_seqlens, device)
+        self.device = device
+        self.grid = int(grid) if grid else msa_default_grid()
+        self.dq_mode = dq_mode
+        self.row_ptr = torch.empty(NUM_INDEX_HEADS * L.NB + 1, dtype=torch.int32, device=device)
+        self.cols = torch.empty(msa_csr_cols_capacity(L), dtype=torch.int32, device=device)
+        self.status = torch.zeros(4, dtype=torch.int32, device=device)
+        self.csr_scratch = _bytes(msa_csr_scratch_bytes(L), device)
+        self.plan = _bytes(msa_plan_bytes(L), device)
+        self.tasks = _bytes(msa_tasks_bytes(L, self.grid), device)
+        self.bwd_scratch = _bytes(msa_bwd_scratch_bytes(L, dq_mode), device)
+        self.Kw = torch.empty((L.W, NUM_KV_HEADS, HEAD_DIM), dtype=torch.bfloat16, device=device)
+        self.Vw = torch.empty_like(self.Kw)
+        self.delta = torch.empty((L.T, NUM_Q_HEADS), dtype=torch.float32, device=device)
+
+    def forward(self, Q, K, V, q2k, scale, O=None, LSE=None, stream=None):
+        """CSR + plan + K/V alignment + forward.  Returns (O, LSE)."""
+        import torch
+        L = self.layout
+        if O is None:
+            O = torch.empty_like(Q)
+        if LSE is None:
+            LSE = torch.empty((L.T, NUM_Q_HEADS), dtype=torch.float32, device=self.device)
+        msa_build_k2q_csr(q2k, L, self.row_ptr, self.cols, self.status, self.csr_scratch, stream)
+        msa_plan(L, q2k, self.plan, stream)
+        msa_align_kv(K, V, L, self.Kw, self.Vw, stream)
+        msa_forward(Q, self.Kw, self.Vw, q2k, L, self.plan, scale, O, LSE, stream)
+        return O, LSE
+
+    def backward(self, Q, dO, O, LSE, scale, dQ=None, dK=None, dV=None, stream=None):
+        """Preprocess + task tables + backward (uses the CSR and K/V workspace of the
+        last forward).  Returns (dQ, dK, dV) in compact order."""
+        import torch
+        L = self.layout
+        if dQ is None:
+            dQ = torch.empty_like(Q)
+        if dK is None:
+            dK = torch.empty((L.T, NUM_KV_HEADS, HEAD_DIM), dtype=torch.bfloat16, device=self.device)
+        if dV is None:
+            dV = torch.empty_like(dK)
+        msa_backward_preprocess(O, dO, L.T, self.delta, stream)
+        msa_build_tasks(L, self.row_ptr, self.cols, self.grid, self.tasks, stream)
+        msa_backward(Q, self.Kw, self.Vw, dO, LSE, self.delta, self.tasks, self.grid, L, scale,
+                     self.dq_mode, dQ, dK, dV, self.bwd_scratch, stream)
+        return dQ, dK, dV
+
+    # ---- views of the integer structures (for checks)
+    def csr(self):
+        rp = self.row_ptr.cpu().numpy()
+        return rp, self.cols[: int(rp[-1])].cpu().numpy()
+
+    def plan_items(self):
+        w = self.plan.view(torch_int32()).cpu().numpy()
+        return w[PLAN_HEADER_WORDS: PLAN_HEADER_WORDS + 4 * int(w[0])].reshape(-1, 4)
+
+    def task_tables(self):
+        w = self.tasks.view(torch_int32()).cpu().numpy()
+        R, grid = int(w[0]), int(w[9])
+        rmax = int(w[10])
+        mo = msa_tasks_meta_offset(grid)
+        meta = w[mo: mo + 4 * rmax].reshape(-1, 4)[:R]
+        qrows = w[mo + 4 * rmax: mo + 12 * rmax].reshape(-1, 8)[:R]
+        qpos = w[mo + 12 * rmax: mo + 20 * rmax].reshape(-1, 8)[:R]
+        cta = w[TASKS_HEADER_WORDS: TASKS_HEADER_WORDS + 4 * (grid + 1)].reshape(4, grid + 1)
+        return dict(R=R, head_rows=w[1:5].copy(), head_first=w[5:9].copy(), grid=grid, meta=meta,
+                    qrows=qrows, qpos=qpos, cta=cta)
+
+
+def torch_int32():
+    import torch
+    return torch.int32

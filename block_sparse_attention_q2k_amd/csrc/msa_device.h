@@ -1,0 +1,80 @@
+// msa_device.h -- device-side helpers shared by the libmsa kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/msa.h"
+
+namespace msa {
+
+constexpr int kH = MSA_NUM_Q_HEADS;         // 64 query heads
+constexpr int kHKV = MSA_NUM_KV_HEADS;      // 4 KV heads
+constexpr int kHI = MSA_NUM_INDEX_HEADS;    // 4 index heads
+constexpr int kD = MSA_HEAD_DIM;            // 128
+constexpr int kBlk = MSA_BLOCK;             // 128 keys per block
+constexpr int kTopk = MSA_TOPK;             // 16 slots
+constexpr int kHPI = kH / kHI;              // 16 query heads per index head
+constexpr int kTileQ = MSA_TILE_QUERIES;    // 8 queries per backward task row
+constexpr int kFwdGroup = MSA_FWD_GROUP;    // queries per forward work item
+constexpr int kTasksHeaderWords = 64;
+constexpr int kPlanHeaderWords = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Largest d with a[d] <= x over a sorted array a[0..n] (a[0] <= x assumed).
+__device__ inline int upper_index(const int32_t *a, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (a[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Round-to-nearest-even fp32 -> bf16 (the gfx950 conversion instruction rounds RNE).
+__device__ inline uint16_t f2bf(float x) {
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+__device__ inline float bf2f(uint16_t u) { return __builtin_bit_cast(float, (uint32_t)u << 16); }
+
+// v_mfma_f32_16x16x32_bf16: C[16x16] += A[16x32] * B[32x16].
+// Lane l: A row l%16, k = 8*(l/16)+0..7; B column l%16, same k; C column l%16,
+// rows 4*(l/16)+0..3.
+__device__ inline f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS access helpers.  `lds` is the byte offset inside the kernel's LDS block.
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j supplies the address of
+// 4 consecutive 16-bit values in[j][0..3]; lane l receives in[4e + l/4][l%4], e=0..3.
+// With lane j pointing at X[k0 + j/4][c0 + 4*(j%4)], lane l gets X[k0 + e][c0 + l].
+__device__ inline bf16x4 lds_read_tr(const lds_char *base, uint32_t byte_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(base + byte_off));
+}
+
+__device__ inline bf16x8 cat8(const bf16x4 &a, const bf16x4 &b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// 16-byte-chunk swizzle for a [rows][256 B] bf16 tile: chunk c of row r is stored at
+// chunk c ^ (r & 15), so 16 lanes reading one chunk of 16 consecutive rows hit 16
+// different chunks.
+__device__ inline uint32_t swz(int row, int byte_in_row) {
+  return (uint32_t)(row * 256 + ((((byte_in_row >> 4) ^ (row & 15)) << 4) | (byte_in_row & 15)));
+}
+
+}  // namespace msa

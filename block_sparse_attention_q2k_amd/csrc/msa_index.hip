@@ -1,0 +1,485 @@
+// msa_index.hip -- HBM-bound steps of the MSA path: K/V workspace alignment, the
+// q2k -> k2q CSR inversion, the forward plan, the backward task tables, delta
+// preprocessing, pool zeroing and gradient finalization.
+//
+// Operator reference: "feat(minimax-m3): add SM100 MSA sparse attention with custom
+// backward" (Design, Custom kernel) and the msa_backward_sm100 API page (module
+// summary, run_backward).
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+
+// ------------------------------------------------------------------ generic fill
+__global__ void fill_u32_kernel(uint32_t *__restrict__ p, size_t n, uint32_t v) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  size_t stride = (size_t)gridDim.x * blockDim.x;
+  // 16-byte stores for the bulk, words for the tail
+  size_t n4 = n / 4;
+  u32x4 vv = {v, v, v, v};
+  for (size_t k = i; k < n4; k += stride) ((u32x4 *)p)[k] = vv;
+  for (size_t k = n4 * 4 + i; k < n; k += stride) p[k] = v;
+}
+
+// ------------------------------------------------------------------ K/V alignment
+// One thread per 16-byte chunk of a workspace row (4 heads x 256 B = 64 chunks).
+__global__ void align_kv_kernel(const u32x4 *__restrict__ K, const u32x4 *__restrict__ V,
+                                const int32_t *__restrict__ cu, const int32_t *__restrict__ cu_ws,
+                                int ndocs, int W, u32x4 *__restrict__ Kw, u32x4 *__restrict__ Vw) {
+  size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (size_t)W * 64) return;
+  int w = (int)(gid >> 6), c = (int)(gid & 63);
+  int d = upper_index(cu_ws, ndocs - 1, w);
+  int p = w - cu_ws[d];
+  u32x4 k = {0, 0, 0, 0}, v = {0, 0, 0, 0};
+  if (p < cu[d + 1] - cu[d]) {
+    size_t src = (size_t)(cu[d] + p) * 64 + c;
+    k = K[src];
+    v = V[src];
+  }
+  Kw[gid] = k;
+  Vw[gid] = v;
+}
+
+// ------------------------------------------------------------------ q2k membership
+// Member blocks of one (index head, query) row: ids in [0, blk_t], first listing only.
+// Returns a 16-bit mask of member slots and ORs precondition flags into *flags.
+__device__ inline uint32_t member_mask(const int32_t *__restrict__ row, int blk_t, int32_t *ids,
+                                       int *flags) {
+  const i32x4 *r4 = (const i32x4 *)row;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    i32x4 v = r4[q];
+    ids[4 * q + 0] = v[0];
+    ids[4 * q + 1] = v[1];
+    ids[4 * q + 2] = v[2];
+    ids[4 * q + 3] = v[3];
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < kTopk; ++j) {
+    int b = ids[j];
+    bool ok = (b >= 0) && (b <= blk_t);
+    if (b != -1 && !ok) *flags |= MSA_Q2K_OUT_OF_RANGE;
+    bool dup = false;
+#pragma unroll
+    for (int jj = 0; jj < j; ++jj) dup |= (ids[jj] == b);
+    if (ok && dup) *flags |= MSA_Q2K_DUPLICATE;
+    if (ok && !dup) m |= 1u << j;
+  }
+  return m;
+}
+
+// CSR count (pass 0) and fill (pass 1): one thread per (index head, query).
+template <int kPass>
+__global__ void csr_kernel(const int32_t *__restrict__ q2k, const int32_t *__restrict__ cu,
+                           const int32_t *__restrict__ cu_ws, int ndocs, int T, int NB,
+                           int32_t *__restrict__ counter, int32_t *__restrict__ cols,
+                           int32_t *__restrict__ status) {
+  int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= kHI * T) return;
+  int i = gid / T, t = gid - i * T;
+  int d = upper_index(cu, ndocs - 1, t);
+  int pos = t - cu[d];
+  int gb0 = cu_ws[d] / kBlk;
+  int32_t ids[kTopk];
+  int flags = 0;
+  uint32_t m = member_mask(q2k + (size_t)gid * kTopk, pos / kBlk, ids, &flags);
+  if (kPass == 0 && flags) atomicOr(status, flags);
+  int rbase = i * NB + gb0;
+#pragma unroll
+  for (int j = 0; j < kTopk; ++j) {
+    if (!((m >> j) & 1)) continue;
+    int r = rbase + ids[j];
+    if (kPass == 0) {
+      atomicAdd(&counter[r], 1);
+    } else {
+      int slot = atomicAdd(&counter[r], 1);
+      cols[slot] = t;
+    }
+  }
+}
+
+// Single-workgroup exclusive scan of n counts: out[0..n] (out[n] = total).  If
+// `copy` is non-null it receives out[0..n-1] as well.  If `tiles` is set the scanned
+// quantity is ceil(in / 8).
+__global__ void __launch_bounds__(1024)
+scan_kernel(const int32_t *__restrict__ in, int n, int tiles, int32_t *__restrict__ out,
+            int32_t *__restrict__ copy) {
+  __shared__ int32_t part[1024];
+  int tid = threadIdx.x, nt = blockDim.x;
+  int per = (n + nt - 1) / nt;
+  int lo = min(n, tid * per), hi = min(n, lo + per);
+  int s = 0;
+  for (int k = lo; k < hi; ++k) s += tiles ? (in[k] + kTileQ - 1) / kTileQ : in[k];
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < nt; off <<= 1) {  // Hillis-Steele inclusive scan
+    int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - s;
+  for (int k = lo; k < hi; ++k) {
+    int v = tiles ? (in[k] + kTileQ - 1) / kTileQ : in[k];  // read before `copy` may alias `in`
+    out[k] = run;
+    if (copy) copy[k] = run;
+    run += v;
+  }
+  if (tid == nt - 1) out[n] = part[nt - 1];
+}
+
+// Row lengths of the CSR from its row pointer.
+__global__ void row_len_kernel(const int32_t *__restrict__ row_ptr, int n, int32_t *__restrict__ len) {
+  int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < n) len[r] = row_ptr[r + 1] - row_ptr[r];
+}
+
+// ------------------------------------------------------------------ forward plan
+// plan layout (int32): [0] items, [1] groups per head G, [2] Gmax; items at
+// [16 + 4p]; aux: gstart [ndocs+1] at aux0, group info {t0,n,d,_} x Gmax at aux1,
+// cost [4 x Gmax] at aux2.
+__global__ void __launch_bounds__(1024)
+plan_groups_kernel(const int32_t *__restrict__ cu, int ndocs, int Gmax, int32_t *__restrict__ plan,
+                   int32_t *__restrict__ gstart) {
+  __shared__ int32_t part[1024];
+  int tid = threadIdx.x, nt = blockDim.x;
+  int per = (ndocs + nt - 1) / nt;
+  int lo = min(ndocs, tid * per), hi = min(ndocs, lo + per);
+  int s = 0;
+  for (int d = lo; d < hi; ++d) s += (cu[d + 1] - cu[d] + kFwdGroup - 1) / kFwdGroup;
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < nt; off <<= 1) {
+    int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - s;
+  for (int d = lo; d < hi; ++d) {
+    gstart[d] = run;
+    run += (cu[d + 1] - cu[d] + kFwdGroup - 1) / kFwdGroup;
+  }
+  if (tid == nt - 1) {
+    int G = part[nt - 1];
+    gstart[ndocs] = G;
+    plan[0] = kHI * G;
+    plan[1] = G;
+    plan[2] = Gmax;
+  }
+}
+
+__global__ void plan_cost_kernel(const int32_t *__restrict__ q2k, const int32_t *__restrict__ cu,
+                                 int ndocs, int T, int Gmax, const int32_t *__restrict__ plan,
+                                 const int32_t *__restrict__ gstart, i32x4 *__restrict__ ginfo,
+                                 int32_t *__restrict__ cost) {
+  int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  int G = plan[1];
+  if (gid >= kHI * G) return;
+  int i = gid / G, g = gid - i * G;
+  int d = upper_index(gstart, ndocs - 1, g);
+  int t0 = cu[d] + (g - gstart[d]) * kFwdGroup;
+  int n = min(kFwdGroup, cu[d + 1] - t0);
+  int c = 0, flags = 0;
+  int32_t ids[kTopk];
+  for (int u = 0; u < n; ++u) {
+    int t = t0 + u;
+    c += __popc(member_mask(q2k + ((size_t)i * T + t) * kTopk, (t - cu[d]) / kBlk, ids, &flags));
+  }
+  cost[i * Gmax + g] = c;
+  if (i == 0) ginfo[g] = i32x4{t0, n, d, 0};
+}
+
+// One workgroup per index head: stable counting sort of its groups by cost,
+// descending; item p = rank * 4 + i.
+__global__ void __launch_bounds__(1024)
+plan_sort_kernel(int Gmax, int32_t *__restrict__ plan, const i32x4 *__restrict__ ginfo,
+                 const int32_t *__restrict__ cost) {
+  constexpr int kMaxCost = kFwdGroup * kTopk;
+  __shared__ int32_t hist[kMaxCost + 1];
+  __shared__ int32_t start[kMaxCost + 1];
+  __shared__ int32_t chunk[1024];
+  int i = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  int G = plan[1];
+  const int32_t *c = cost + (size_t)i * Gmax;
+  for (int k = tid; k <= kMaxCost; k += nt) hist[k] = 0;
+  __syncthreads();
+  for (int g = tid; g < G; g += nt) atomicAdd(&hist[c[g]], 1);
+  __syncthreads();
+  if (tid == 0) {  // start[v] = number of groups with cost > v
+    int run = 0;
+    for (int v = kMaxCost; v >= 0; --v) {
+      start[v] = run;
+      run += hist[v];
+    }
+  }
+  __syncthreads();
+  for (int base = 0; base < G; base += nt) {
+    int g = base + tid;
+    int my = g < G ? c[g] : -1;
+    chunk[tid] = my;
+    __syncthreads();
+    if (g < G) {
+      int before = 0;
+      for (int j = 0; j < tid; ++j) before += (chunk[j] == my);
+      int rank = start[my] + before;
+      i32x4 gi = ginfo[g];
+      ((i32x4 *)(plan + kPlanHeaderWords))[rank * kHI + i] = i32x4{i, gi[0], gi[1], gi[2]};
+    }
+    __syncthreads();
+    // advance the per-cost starts by this chunk's counts
+    if (g < G) {
+      int last = 1;
+      for (int j = tid + 1; j < nt && base + j < G; ++j) last &= (chunk[j] != my);
+      if (last) {
+        int cnt = 0;
+        for (int j = 0; j <= tid; ++j) cnt += (chunk[j] == my);
+        start[my] += cnt;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ task tables
+// Header, per-head row counts and CTA bounds from the scanned tile offsets.
+__global__ void __launch_bounds__(1024)
+tasks_header_kernel(const int32_t *__restrict__ tile_off, int NB, int grid, int rmax,
+                    int32_t *__restrict__ tasks) {
+  int tid = threadIdx.x;
+  if (tid == 0) {
+    tasks[0] = tile_off[kHI * NB];
+    for (int i = 0; i < kHI; ++i) {
+      tasks[1 + i] = tile_off[(i + 1) * NB] - tile_off[i * NB];
+      tasks[5 + i] = tile_off[i * NB];
+    }
+    tasks[9] = grid;
+    tasks[10] = rmax;
+  }
+  for (int k = tid; k < kHI * (grid + 1); k += blockDim.x) {
+    int i = k / (grid + 1), c = k - i * (grid + 1);
+    long long rows = tile_off[(i + 1) * NB] - tile_off[i * NB];
+    tasks[kTasksHeaderWords + k] = tile_off[i * NB] + (int)((c * rows) / grid);
+  }
+}
+
+// One thread per CSR entry e: row of bucket r, slot (e - row_ptr[r]) % 8.
+__global__ void tasks_fill_kernel(const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ cols,
+                                  const int32_t *__restrict__ tile_off,
+                                  const int32_t *__restrict__ cu, const int32_t *__restrict__ cu_ws,
+                                  int ndocs, int NB, int cap, i32x4 *__restrict__ meta,
+                                  int32_t *__restrict__ qrows, int32_t *__restrict__ qpos) {
+  int e = blockIdx.x * blockDim.x + threadIdx.x;
+  int nrows = kHI * NB;
+  if (e >= cap || e >= row_ptr[nrows]) return;
+  int r = upper_index(row_ptr, nrows - 1, e);
+  while (r + 1 <= nrows - 1 && row_ptr[r + 1] <= e) ++r;  // skip empty rows sharing e
+  int rel = e - row_ptr[r];
+  int k = rel / kTileQ, s = rel - k * kTileQ;
+  int row = tile_off[r] + k;
+  int gb = r % NB;
+  int d = upper_index(cu_ws, ndocs - 1, gb * kBlk);
+  int t = cols[e];
+  qrows[(size_t)row * kTileQ + s] = t;
+  qpos[(size_t)row * kTileQ + s] = t - cu[d];
+  if (s == 0) {
+    int len = row_ptr[r + 1] - row_ptr[r];
+    int ntile = (len + kTileQ - 1) / kTileQ;
+    int nv = min(kTileQ, len - k * kTileQ);
+    int flags = (k == 0 ? 1 : 0) | (k == ntile - 1 ? 2 : 0);
+    meta[row] = i32x4{r, nv, flags, k};
+    for (int p = nv; p < kTileQ; ++p) {
+      qrows[(size_t)row * kTileQ + p] = -1;
+      qpos[(size_t)row * kTileQ + p] = -1;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ delta
+// delta[t,h] = sum_c dO*O in fp32.  16 lanes per (t, h) row, 8 elements each.
+__global__ void preprocess_kernel(const u32x4 *__restrict__ O, const u32x4 *__restrict__ dO,
+                                  size_t rows, float *__restrict__ delta) {
+  size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  size_t row = gid >> 4;
+  float acc = 0.f;
+  if (row < rows) {
+    u32x4 a = O[gid], b = dO[gid];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc += bf2f((uint16_t)(a[q] & 0xffff)) * bf2f((uint16_t)(b[q] & 0xffff));
+      acc += bf2f((uint16_t)(a[q] >> 16)) * bf2f((uint16_t)(b[q] >> 16));
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  acc += __shfl_xor(acc, 8);
+  if (row < rows && (gid & 15) == 0) delta[row] = acc;
+}
+
+// ------------------------------------------------------------------ finalize
+// Part A (dq_chunks threads): dQ pool -> bf16 dQ, 8 elements per thread.
+// Part B: dK/dV pools (fp32 workspace rows) -> bf16 compact rows, 8 elements per thread.
+__global__ void finalize_kernel(const void *__restrict__ dq_pool, int dq_mode, size_t dq_chunks,
+                                const float *__restrict__ dk_pool, const float *__restrict__ dv_pool,
+                                const int32_t *__restrict__ cu, const int32_t *__restrict__ cu_ws,
+                                int ndocs, int T, u32x4 *__restrict__ dQ, u32x4 *__restrict__ dK,
+                                u32x4 *__restrict__ dV) {
+  size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid < dq_chunks) {
+    if (dq_mode == MSA_DQ_ACCUM_FP32) {
+      const f32x4 *p = (const f32x4 *)dq_pool + 2 * gid;
+      f32x4 a = p[0], b = p[1];
+      dQ[gid] = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                      pack_bf16x2(b[2], b[3])};
+    } else {
+      dQ[gid] = ((const u32x4 *)dq_pool)[gid];
+    }
+    return;
+  }
+  size_t k = gid - dq_chunks;
+  if (k >= (size_t)T * kHKV * kD / 8) return;
+  int t = (int)(k / (kHKV * kD / 8));
+  int c = (int)(k - (size_t)t * (kHKV * kD / 8));
+  int d = upper_index(cu, ndocs - 1, t);
+  size_t w = (size_t)(cu_ws[d] + t - cu[d]);
+  const f32x4 *pk = (const f32x4 *)(dk_pool + w * kHKV * kD) + 2 * c;
+  const f32x4 *pv = (const f32x4 *)(dv_pool + w * kHKV * kD) + 2 * c;
+  f32x4 a = pk[0], b = pk[1];
+  dK[k] = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                pack_bf16x2(b[2], b[3])};
+  a = pv[0];
+  b = pv[1];
+  dV[k] = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                pack_bf16x2(b[2], b[3])};
+}
+
+// ================================================================== host launchers
+namespace host {
+
+static inline unsigned blocks_for(size_t n, unsigned bs) { return (unsigned)((n + bs - 1) / bs); }
+
+hipError_t fill_u32(void *p, size_t n, uint32_t v, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t work = (n + 3) / 4;
+  unsigned nb = blocks_for(work, 256);
+  if (nb > 8192) nb = 8192;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(nb), dim3(256), 0, s, (uint32_t *)p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t align_kv(const void *K, const void *V, const LayoutArgs &L, void *Kw, void *Vw,
+                    hipStream_t s) {
+  size_t n = (size_t)L.W * 64;
+  hipLaunchKernelGGL(align_kv_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s, (const u32x4 *)K,
+                     (const u32x4 *)V, L.cu, L.cu_ws, L.ndocs, L.W, (u32x4 *)Kw, (u32x4 *)Vw);
+  return hipGetLastError();
+}
+
+hipError_t build_csr(const int32_t *q2k, const LayoutArgs &L, int32_t *row_ptr, int32_t *cols,
+                     int32_t *status, int32_t *counter, hipStream_t s) {
+  int nrows = kHI * L.NB;
+  hipError_t e = fill_u32(counter, nrows, 0, s);
+  if (e != hipSuccess) return e;
+  e = fill_u32(status, 1, 0, s);
+  if (e != hipSuccess) return e;
+  unsigned nb = blocks_for((size_t)kHI * L.T, 256);
+  hipLaunchKernelGGL(csr_kernel<0>, dim3(nb), dim3(256), 0, s, q2k, L.cu, L.cu_ws, L.ndocs, L.T,
+                     L.NB, counter, cols, status);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, counter, nrows, 0, row_ptr, counter);
+  hipLaunchKernelGGL(csr_kernel<1>, dim3(nb), dim3(256), 0, s, q2k, L.cu, L.cu_ws, L.ndocs, L.T,
+                     L.NB, counter, cols, status);
+  return hipGetLastError();
+}
+
+size_t plan_gmax(const LayoutArgs &L) { return (size_t)(L.T + kFwdGroup - 1) / kFwdGroup + L.ndocs; }
+
+size_t plan_bytes(const LayoutArgs &L) {
+  size_t gmax = plan_gmax(L);
+  size_t words = kPlanHeaderWords + 4 * kHI * gmax  // items
+                 + ((L.ndocs + 1 + 3) / 4) * 4      // gstart
+                 + 4 * gmax                         // group info
+                 + kHI * gmax;                      // cost
+  return words * 4;
+}
+
+hipError_t build_plan(const LayoutArgs &L, const int32_t *q2k, void *plan_v, hipStream_t s) {
+  int32_t *plan = (int32_t *)plan_v;
+  int gmax = (int)plan_gmax(L);
+  int32_t *gstart = plan + kPlanHeaderWords + 4 * kHI * gmax;
+  i32x4 *ginfo = (i32x4 *)(gstart + ((L.ndocs + 1 + 3) / 4) * 4);
+  int32_t *cost = (int32_t *)(ginfo + gmax);
+  hipLaunchKernelGGL(plan_groups_kernel, dim3(1), dim3(1024), 0, s, L.cu, L.ndocs, gmax, plan, gstart);
+  hipLaunchKernelGGL(plan_cost_kernel, dim3(blocks_for((size_t)kHI * gmax, 128)), dim3(128), 0, s,
+                     q2k, L.cu, L.ndocs, L.T, gmax, plan, gstart, ginfo, cost);
+  hipLaunchKernelGGL(plan_sort_kernel, dim3(kHI), dim3(1024), 0, s, gmax, plan, ginfo, cost);
+  return hipGetLastError();
+}
+
+size_t tasks_rmax(const LayoutArgs &L) {
+  return (size_t)kHI * L.T * kTopk / kTileQ + (size_t)kHI * L.NB;
+}
+size_t tasks_meta_offset_words(int grid) {
+  size_t w = kTasksHeaderWords + (size_t)kHI * (grid + 1);
+  return (w + 63) / 64 * 64;
+}
+size_t tasks_bytes(const LayoutArgs &L, int grid) {
+  size_t rmax = tasks_rmax(L);
+  size_t words = tasks_meta_offset_words(grid) + 4 * rmax + 2 * kTileQ * rmax  // meta, qrows, qpos
+                 + 2 * ((size_t)kHI * L.NB + 1) + 64;                        // lengths, tile_off
+  return words * 4;
+}
+
+TaskView task_view(const LayoutArgs &L, int grid, void *tasks_v) {
+  TaskView v;
+  int32_t *tasks = (int32_t *)tasks_v;
+  size_t rmax = tasks_rmax(L);
+  v.header = tasks;
+  v.cta = tasks + kTasksHeaderWords;
+  v.meta = tasks + tasks_meta_offset_words(grid);
+  v.qrows = v.meta + 4 * rmax;
+  v.qpos = v.qrows + kTileQ * rmax;
+  v.len = v.qpos + kTileQ * rmax;
+  v.tile_off = v.len + ((size_t)kHI * L.NB + 1);
+  v.rmax = rmax;
+  return v;
+}
+
+hipError_t build_tasks(const LayoutArgs &L, const int32_t *row_ptr, const int32_t *cols, int grid,
+                       void *tasks_v, hipStream_t s) {
+  TaskView v = task_view(L, grid, tasks_v);
+  int nrows = kHI * L.NB;
+  hipLaunchKernelGGL(row_len_kernel, dim3(blocks_for(nrows, 256)), dim3(256), 0, s, row_ptr, nrows,
+                     v.len);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, v.len, nrows, 1, v.tile_off,
+                     (int32_t *)nullptr);
+  hipLaunchKernelGGL(tasks_header_kernel, dim3(1), dim3(1024), 0, s, v.tile_off, L.NB, grid,
+                     (int)v.rmax, v.header);
+  size_t cap = (size_t)kHI * L.T * kTopk;
+  hipLaunchKernelGGL(tasks_fill_kernel, dim3(blocks_for(cap, 256)), dim3(256), 0, s, row_ptr, cols,
+                     v.tile_off, L.cu, L.cu_ws, L.ndocs, L.NB, (int)cap, (i32x4 *)v.meta, v.qrows,
+                     v.qpos);
+  return hipGetLastError();
+}
+
+hipError_t preprocess(const void *O, const void *dO, int T, float *delta, hipStream_t s) {
+  size_t rows = (size_t)T * kH;
+  hipLaunchKernelGGL(preprocess_kernel, dim3(blocks_for(rows * 16, 256)), dim3(256), 0, s,
+                     (const u32x4 *)O, (const u32x4 *)dO, rows, delta);
+  return hipGetLastError();
+}
+
+hipError_t finalize(const void *dq_pool, int mode, const float *dk_pool, const float *dv_pool,
+                    const LayoutArgs &L, void *dQ, void *dK, void *dV, hipStream_t s) {
+  size_t dq_chunks = (size_t)L.T * kH * kD / 8;
+  size_t kv_chunks = (size_t)L.T * kHKV * kD / 8;
+  hipLaunchKernelGGL(finalize_kernel, dim3(blocks_for(dq_chunks + kv_chunks, 256)), dim3(256), 0, s,
+                     dq_pool, mode, dq_chunks, dk_pool, dv_pool, L.cu, L.cu_ws, L.ndocs, L.T,
+                     (u32x4 *)dQ, (u32x4 *)dK, (u32x4 *)dV);
+  return hipGetLastError();
+}
+
+}  // namespace host
+}  // namespace msa

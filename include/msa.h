@@ -1,0 +1,216 @@
+/*
+ * msa.h -- C ABI of libmsa, an MI355X (gfx950) implementation of MiniMax Sparse
+ * Attention (MSA) prefill forward and backward.
+ *
+ * The operator ("feat(minimax-m3): add SM100 MSA sparse attention with custom
+ * backward", sections Design and Supported scope) is causal, document-local, top-k
+ * block-sparse GQA attention with a fixed topology: 64 query heads, 4 KV heads,
+ * 4 index heads, head dim 128, key blocks of 128 tokens and 16 selection slots per
+ * (index head, query).  Query head h belongs to index head h / 16, which reads KV
+ * head h / 16.  Token t of document d = doc(t) attends to the keys s of the same
+ * document with pos(s) <= pos(t) whose block pos(s) / 128 is listed in
+ * q2k[h / 16][t][0..15]; -1 marks an unused slot.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless the name ends in _host.  All device arrays
+ *     are dense, row-major, 16-byte aligned, on the device that is current when the
+ *     call is made.  The caller owns every buffer, including scratch; the library
+ *     allocates nothing and keeps no per-call state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls
+ *     only enqueue work on it; none synchronizes the host.
+ *   - Return value: MSA_OK (0) or an MSA_ERR_* code.  Argument errors are detected on
+ *     the host before anything is enqueued; nothing is written in that case.
+ *   - bf16 values are passed as uint16_t bit patterns (msa_bf16).
+ *   - Results that use atomics (msa_backward, the CSR column order) are not bitwise
+ *     reproducible run to run (pull-request page, Supported scope: atomic
+ *     accumulation, not bitwise deterministic).
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Fixed topology (pull-request page, Supported scope). */
+#define MSA_NUM_Q_HEADS 64
+#define MSA_NUM_KV_HEADS 4
+#define MSA_NUM_INDEX_HEADS 4
+#define MSA_HEAD_DIM 128
+#define MSA_BLOCK 128
+#define MSA_TOPK 16
+/* Backward task row: 8 queries x 16 heads = 128 rows (msa_backward_sm100 API page,
+ * module summary). */
+#define MSA_TILE_QUERIES 8
+/* Forward work item: up to this many consecutive queries of one document. */
+#define MSA_FWD_GROUP 16
+
+typedef uint16_t msa_bf16;
+
+enum {
+  MSA_OK = 0,
+  MSA_ERR_NULL = 1,      /* a required pointer is NULL */
+  MSA_ERR_ALIGN = 2,     /* a device pointer is not 16-byte aligned */
+  MSA_ERR_SHAPE = 3,     /* inconsistent sizes or layout */
+  MSA_ERR_SCRATCH = 4,   /* a caller buffer is smaller than its *_bytes query */
+  MSA_ERR_MODE = 5,      /* unknown dQ accumulation mode */
+  MSA_ERR_GRID = 6,      /* grid outside [1, MSA_MAX_GRID] */
+  MSA_ERR_LAUNCH = 7,    /* a kernel launch failed */
+  MSA_ERR_DEVICE = 8     /* no usable gfx950 device current */
+};
+
+/* Bits of the device status word written by msa_build_k2q_csr. */
+enum {
+  MSA_Q2K_OUT_OF_RANGE = 1, /* an id outside [-1, blk(t)] (ignored) */
+  MSA_Q2K_DUPLICATE = 2     /* an id listed twice for one (index head, query) (ignored) */
+};
+
+/* dQ accumulation pool of msa_backward (pull-request page, Supported scope: dQ takes
+ * 16-bit atomic accumulation, dK/dV FP32). */
+enum { MSA_DQ_ACCUM_FP32 = 0, MSA_DQ_ACCUM_BF16X2 = 1 };
+
+#define MSA_MAX_GRID 4096
+
+/*
+ * Packed-document layout (pull-request page, Design: the layout carries document
+ * offsets and token coordinates; every document is padded to a multiple of 128 tokens
+ * in the attention K/V workspace).  A host struct holding device arrays:
+ *   cu_seqlens [num_docs + 1]: 0 = cu[0] < cu[1] < ... < cu[N] = num_tokens;
+ *     document d owns compact tokens [cu[d], cu[d+1]).
+ *   cu_ws [num_docs + 1]: cu_ws[d] = sum over e < d of 128 * ceil(L_e / 128), so
+ *     document d owns workspace rows [cu_ws[d], cu_ws[d+1]); num_ws_tokens = cu_ws[N].
+ * The device arrays must hold what msa_layout_host returns for the same offsets.
+ */
+typedef struct {
+  int32_t num_docs;
+  int32_t num_tokens;
+  int32_t num_ws_tokens;
+  const int32_t *cu_seqlens;
+  const int32_t *cu_ws;
+} msa_layout;
+
+/* Host: validates cu_seqlens_host [num_docs + 1] (starts at 0, strictly increasing)
+ * and writes cu_ws_host [num_docs + 1] and *num_ws_tokens.  MSA_ERR_SHAPE otherwise. */
+int msa_layout_host(const int32_t *cu_seqlens_host, int32_t num_docs, int32_t *cu_ws_host,
+                    int32_t *num_ws_tokens);
+
+/* ---------------------------------------------------------------------------------
+ * Size queries (pure host functions; 0 means the layout is invalid).
+ * --------------------------------------------------------------------------------- */
+/* Bytes of the CSR scratch (per-row counters). */
+size_t msa_csr_scratch_bytes(const msa_layout *layout);
+/* Capacity (int32 elements) that `cols` must have: 4 * T * 16. */
+size_t msa_csr_cols_capacity(const msa_layout *layout);
+/* Bytes of the forward plan buffer. */
+size_t msa_plan_bytes(const msa_layout *layout);
+/* Bytes of the backward task buffer for a grid of `grid` workgroups. */
+size_t msa_tasks_bytes(const msa_layout *layout, int32_t grid);
+/* Bytes of the backward scratch (dQ pool in `dq_accum_mode`, fp32 dK/dV pools). */
+size_t msa_bwd_scratch_bytes(const msa_layout *layout, int dq_accum_mode);
+/* Grid size msa_build_tasks / msa_backward use by default (one workgroup per CU). */
+int32_t msa_default_grid(void);
+
+/* ---------------------------------------------------------------------------------
+ * K/V workspace alignment (pull-request page, Design: K/V workspaces with each
+ * document padded to a multiple of 128 tokens; msa_backward_sm100 API page,
+ * run_backward: W a positive multiple of 128).
+ *   K, V: bf16 [T, 4, 128] compact.  Kw, Vw: bf16 [W, 4, 128]; row cu_ws[d] + p holds
+ *   compact row cu[d] + p for p < L_d and zeros after.
+ * --------------------------------------------------------------------------------- */
+int msa_align_kv(const msa_bf16 *K, const msa_bf16 *V, const msa_layout *layout,
+                 msa_bf16 *Kw, msa_bf16 *Vw, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * q2k -> k2q CSR inversion (pull-request page, Design: forward-derived CSR; bindings
+ * page: build_k2q_csr).
+ *   q2k: int32 [4, T, 16].  Row r = i * NB + gb (NB = W / 128) lists the queries t
+ *   whose index head i selects workspace block gb = cu_ws[doc(t)] / 128 + b.
+ *   row_ptr: int32 [4 * NB + 1] (exclusive prefix of row lengths).  cols: int32
+ *   [msa_csr_cols_capacity]; row r's queries at cols[row_ptr[r] .. row_ptr[r+1]) in
+ *   unspecified order.  Slots that are -1, outside [0, blk(t)] or repeat an earlier
+ *   slot of the same row are skipped; the latter two set MSA_Q2K_* bits in *status
+ *   (device int32, overwritten by this call).
+ * --------------------------------------------------------------------------------- */
+int msa_build_k2q_csr(const int32_t *q2k, const msa_layout *layout, int32_t *row_ptr,
+                      int32_t *cols, int32_t *status, void *scratch, size_t scratch_bytes,
+                      void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Forward plan (the forward schedule; bindings page: fmha_sm100_plan).  Cuts every
+ * document into groups of MSA_FWD_GROUP consecutive queries; each (index head, group)
+ * is one work item.  Items of one head are ordered by cost (member slots) descending,
+ * ties in document order, and heads are interleaved: item p belongs to head p % 4.
+ * Layout of `plan` (int32): plan[0] = item count; items at plan[16 + 4p] = {i, t0, n,
+ * doc}.  q2k as above.
+ * --------------------------------------------------------------------------------- */
+int msa_plan(const msa_layout *layout, const int32_t *q2k, void *plan, size_t plan_bytes,
+             void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Forward (pull-request page, Design: Q[T,64,128], K/V, q2k -> O[T,64,128] + LSE).
+ *   Q: bf16 [T, 64, 128].  Kw, Vw: bf16 [W, 4, 128] from msa_align_kv.  q2k as above.
+ *   O: bf16 [T, 64, 128].  LSE: fp32 [T, 64], natural log of the sum of exp(scores),
+ *   scores including `scale`; -inf (and O = 0) for a row with no keys.
+ * --------------------------------------------------------------------------------- */
+int msa_forward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, const int32_t *q2k,
+                const msa_layout *layout, const void *plan, float scale, msa_bf16 *O,
+                float *LSE, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Backward preprocessing (pull-request page, Custom kernel: delta preprocessing).
+ *   delta[t, h] = sum_c dO[t,h,c] * O[t,h,c] in fp32 from the bf16 O and dO [T,64,128].
+ * --------------------------------------------------------------------------------- */
+int msa_backward_preprocess(const msa_bf16 *O, const msa_bf16 *dO, int32_t num_tokens,
+                            float *delta, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Backward task tables + CTA walk (pull-request page, Changelog / Custom kernel: task
+ * construction from the saved forward schedule with exact counts and device-side CTA
+ * scheduling; msa_backward_sm100 API page: 128-row tiles of 8 queries x 16 heads
+ * bucketed by (index head, key block)).  From the CSR: bucket r holds
+ * ceil(len_r / 8) task rows, every one full except the last.  Layout of `tasks`
+ * (int32 words):
+ *   [0] R (total rows), [1..4] rows per index head, [5..8] first row of each head,
+ *   [9] grid, [10] row capacity Rmax;
+ *   cta bounds at [64 ...]: (4 * (grid + 1)) words, workgroup c walks rows
+ *     [cta[i*(grid+1)+c], cta[i*(grid+1)+c+1]) of index head i, = first_i +
+ *     floor(c * rows_i / grid);
+ *   meta at word msa_tasks_meta_offset(): Rmax x {r, n_valid, flags, k} (flags bit0 =
+ *     first row of its bucket, bit1 = last);
+ *   qrows then qpos: Rmax x 8 int32 each (query ids; document-local positions; -1 pad).
+ * Rows inside one bucket appear in ascending k; their query sets follow the CSR order.
+ * --------------------------------------------------------------------------------- */
+size_t msa_tasks_meta_offset(int32_t grid);
+int msa_build_tasks(const msa_layout *layout, const int32_t *row_ptr, const int32_t *cols,
+                    int32_t grid, void *tasks, size_t tasks_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Backward (msa_backward_sm100 API page, run_backward and module summary):
+ *   Q, dO: bf16 [T, 64, 128]; Kw, Vw: bf16 [W, 4, 128]; LSE: fp32 [T, 64] from
+ *   msa_forward; delta from msa_backward_preprocess; tasks from msa_build_tasks and
+ *   `grid` the value it was built with (the launch uses that many workgroups).  Writes dQ bf16 [T, 64, 128] and dK, dV bf16 [T, 4, 128] in
+ *   compact token order.  scratch >= msa_bwd_scratch_bytes(layout, dq_accum_mode):
+ *   the dQ pool (fp32 or bf16) and fp32 dK/dV pools, zeroed by this call.
+ * --------------------------------------------------------------------------------- */
+int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, const msa_bf16 *dO,
+                 const float *LSE, const float *delta, const void *tasks, int32_t grid,
+                 const msa_layout *layout, float scale, int dq_accum_mode, msa_bf16 *dQ,
+                 msa_bf16 *dK, msa_bf16 *dV, void *scratch, size_t scratch_bytes,
+                 void *stream);
+
+/* Timing hook: if both are non-NULL hipEvent_t handles, every later msa_backward call
+ * from this host thread records `start` right before its main KV-parallel kernel and
+ * `stop` right after it, on the call's stream (NULL, NULL turns it off).  Lets a caller
+ * time that kernel alone with hipEventElapsedTime. */
+void msa_set_backward_timing_events(void *start, void *stop);
+
+/* Short description of a return code. */
+const char *msa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_H_ */

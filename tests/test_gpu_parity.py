@@ -1,0 +1,117 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Integer structures (CSR, plan, task tables) bit-exact; O, LSE, dQ, dK, dV within
+relative L2 <= 1e-2 and max-abs <= 3e-2 of the oracle's largest magnitude; delta
+(fp32 from the bf16 O) within 1e-5 relative L2 of the fp64 sum over the same O."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as WL
+from oracle import oracle as OR
+from _gpu_util import (SCALE, check_close, check_lse, check_structures, inputs64, run_gpu, say,
+                       to_np)
+
+pytestmark = pytest.mark.gpu
+
+# small layouts spanning several tiles, ragged tails and several documents
+SMALL = {
+    "dense_512": ([512], "all", 0),
+    "uniform_3docs_ragged": ([700, 300, 129], "uniform", 1),
+    "sink_1000": ([1000], "sink", 2),
+    "local_decay_2100": ([2100], "local_decay", 3),
+    "zipf_many_short": ([300, 17, 129, 128, 64, 255, 1, 40], "zipf", 4),
+}
+
+
+def _small(name, scatter=False):
+    lens, rule, seed = SMALL[name]
+    cu, q2k = WL.make_custom(lens, rule, seed)
+    if scatter:
+        q2k = WL.scatter_unused(q2k, seed)
+    tens = WL.make_tensors(int(cu[-1]), 100 + seed)
+    return cu, q2k, tens
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_structures_small(name):
+    say("case", name)
+    cu, q2k, tens = _small(name, scatter=True)
+    m, _ = run_gpu(cu, q2k, tens, backward=True, grid=37)
+    assert check_structures(m, cu, q2k) == 0
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_parity_small(name):
+    say("case", name)
+    cu, q2k, tens = _small(name)
+    m, out = run_gpu(cu, q2k, tens, backward=False)
+    Q, K, V, _ = inputs64(tens)
+    O, LSE = OR.forward(Q, K, V, q2k, cu, SCALE)
+    check_close("O", to_np(out["O"]), O)
+    check_lse(to_np(out["LSE"]), LSE)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_backward_parity_small(name, mode):
+    say("case", name, "dq mode", mode)
+    cu, q2k, tens = _small(name, scatter=(mode == 1))
+    m, out = run_gpu(cu, q2k, tens, mode=mode)
+    Q, K, V, dO = inputs64(tens)
+    dQ, dK, dV, _, _ = OR.backward(Q, K, V, dO, q2k, cu, SCALE)
+    # delta from the bf16 O the backward consumes, fp32 on the GPU vs fp64 here
+    dref = OR.delta(to_np(out["O"]), dO)
+    check_close("delta", to_np(out["delta"]), dref, rel_l2=1e-5, max_abs_frac=1e-5)
+    check_close("dQ", to_np(out["dQ"]), dQ)
+    check_close("dK", to_np(out["dK"]), dK)
+    check_close("dV", to_np(out["dV"]), dV)
+
+
+def test_invalid_ids_flagged_and_ignored():
+    """Out-of-range and repeated ids set the status bits and add no keys."""
+    cu, q2k, tens = _small("uniform_3docs_ragged")
+    bad = q2k.copy()
+    T = int(cu[-1])
+    doc = np.searchsorted(cu, np.arange(T), "right") - 1
+    blk = (np.arange(T) - cu[doc]) // 128
+    for t in range(0, T, 7):
+        free = np.nonzero(bad[0, t] == -1)[0]
+        if len(free) >= 2:
+            bad[0, t, free[0]] = blk[t] + 1 + t % 5  # beyond the causal range
+            bad[0, t, free[1]] = bad[0, t, 0]          # repeat
+    m, out = run_gpu(cu, bad, tens)
+    assert check_structures(m, cu, bad) == 3
+    m2, ref = run_gpu(cu, q2k, tens)
+    assert torch.equal(out["O"], ref["O"]) and torch.equal(out["LSE"], ref["LSE"])
+    for k in ("dQ", "dK", "dV"):  # atomics: equal up to summation order
+        check_close(k, to_np(out[k]), to_np(ref[k]), rel_l2=1e-4, max_abs_frac=1e-2)
+
+
+def test_empty_key_set_rows():
+    cu, q2k, tens = _small("sink_1000")
+    q2k[1, 5, :] = -1
+    q2k[2, 900, :] = -1
+    m, out = run_gpu(cu, q2k, tens)
+    O, L, dQ = to_np(out["O"]), to_np(out["LSE"]), to_np(out["dQ"])
+    assert np.all(O[5, 16:32] == 0) and np.all(np.isneginf(L[5, 16:32]))
+    assert np.all(O[900, 32:48] == 0) and np.all(dQ[900, 32:48] == 0)
+    Q, K, V, dO = inputs64(tens)
+    rO, rL = OR.forward(Q, K, V, q2k, cu, SCALE)
+    check_close("O", O, rO)
+    check_lse(L, rL)
+
+
+def test_two_calls_reuse_buffers_and_stay_consistent():
+    """The same MSA object run twice gives the same structures and close gradients
+    (atomics make them not bitwise equal)."""
+    cu, q2k, tens = _small("uniform_3docs_ragged")
+    m, out1 = run_gpu(cu, q2k, tens)
+    Q, K, V, dO = (tens[k].cuda() for k in ("Q", "K", "V", "dO"))
+    q = torch.from_numpy(q2k).cuda()
+    O, LSE = m.forward(Q, K, V, q, SCALE)
+    dQ, dK, dV = m.backward(Q, dO, O, LSE, SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(O, out1["O"]) and torch.equal(LSE, out1["LSE"])
+    for a, b, n in ((dQ, out1["dQ"], "dQ"), (dK, out1["dK"], "dK"), (dV, out1["dV"], "dV")):
+        check_close(n, to_np(a), to_np(b), rel_l2=1e-2, max_abs_frac=1e-2)
