@@ -133,6 +133,9 @@ def main():
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for pair in kev:  # torch creates the HIP event on its first record
+        for e in pair:
+            e.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):

@@ -253,33 +253,39 @@ def _dims(Q, K, q2k):
 
 def forward(Q, K, V, q2k, cu_seqlens, scale, rows=None, blk: int = 128):
     """O [T,H,D] (fp64) and LSE [T,H] (natural log, scale included) of the exact
-    forward.  ``rows``: optional boolean [T]; other rows are returned as NaN."""
+    forward.  ``rows``: optional boolean [T]; then only those rows are computed and
+    (O[rows], LSE[rows]) are returned, in ascending row order."""
     Q, K, V = _f64(Q), _f64(K), _f64(V)
     q = _i32(q2k)
     cu = _i32(cu_seqlens)
     T, H, HKV, HI, D, TOPK = _dims(Q, K, q)
-    O = np.full((T, H, D), np.nan)
-    LSE = np.full((T, H), np.nan)
+    # untouched pages of np.empty are never materialised
+    O = np.empty((T, H, D))
+    LSE = np.empty((T, H))
     mask = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.uint8))
     rc = _lib().msa_oracle_forward(T, H, HKV, HI, D, blk, TOPK, len(cu) - 1, _p(cu), _p(Q),
                                    _p(K), _p(V), _p(q), float(scale), _p(mask), _p(O), _p(LSE))
     if rc:
         raise RuntimeError("msa_oracle_forward failed (%d)" % rc)
-    return O, LSE
+    if rows is None:
+        return O, LSE
+    idx = np.nonzero(np.asarray(rows, dtype=bool))[0]
+    return O[idx], LSE[idx]
 
 
 def backward(Q, K, V, dO, q2k, cu_seqlens, scale, q_rows=None, k_tokens=None, blk: int = 128):
     """Exact fp64 gradients (dQ [T,H,D], dK [T,HKV,D], dV [T,HKV,D]) of the exact
     forward, plus its LSE and delta [T,H].  ``q_rows`` selects dQ rows, ``k_tokens``
-    the key tokens whose dK/dV rows are wanted (boolean [T] each; None = all).
-    Unselected outputs are NaN."""
+    the key tokens whose dK/dV rows are wanted (boolean [T] each; None = all); with a
+    selection, dQ[q_rows] / dK[k_tokens] / dV[k_tokens] are returned in ascending token
+    order, and LSE/delta are valid only on rows the selection needed."""
     Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
     q = _i32(q2k)
     cu = _i32(cu_seqlens)
     T, H, HKV, HI, D, TOPK = _dims(Q, K, q)
-    dQ = np.full((T, H, D), np.nan)
-    dK = np.full((T, HKV, D), np.nan)
-    dV = np.full((T, HKV, D), np.nan)
+    dQ = np.empty((T, H, D))
+    dK = np.empty((T, HKV, D))
+    dV = np.empty((T, HKV, D))
     LSE = np.empty((T, H))
     dl = np.empty((T, H))
     qm = None if q_rows is None else np.ascontiguousarray(np.asarray(q_rows, dtype=np.uint8))
@@ -289,6 +295,11 @@ def backward(Q, K, V, dO, q2k, cu_seqlens, scale, q_rows=None, k_tokens=None, bl
                                     _p(dQ), _p(dK), _p(dV), _p(LSE), _p(dl))
     if rc:
         raise RuntimeError("msa_oracle_backward failed (%d)" % rc)
+    if q_rows is not None:
+        dQ = dQ[np.nonzero(np.asarray(q_rows, dtype=bool))[0]]
+    if k_tokens is not None:
+        kidx = np.nonzero(np.asarray(k_tokens, dtype=bool))[0]
+        dK, dV = dK[kidx], dV[kidx]
     return dQ, dK, dV, LSE, dl
 
 
