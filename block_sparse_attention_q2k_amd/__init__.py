@@ -47,6 +47,10 @@ def lib():
     """Load libmsa.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
+        # torch bundles its own HIP runtime (soname libamdhip64.so.7) and its libraries
+        # request it by the unversioned name; loading it first makes libmsa bind to
+        # that same runtime instead of a second copy (which would crash the process).
+        import torch  # noqa: F401
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError("libmsa.so is not built (%s); run block_sparse_attention_q2k_amd.build"
                                % _LIB_PATH)
