@@ -81,7 +81,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--dq-mode", choices=["fp32", "bf16x2"], default="bf16x2")
+    ap.add_argument("--dq-mode", choices=["recompute", "fp32", "bf16x2"], default="recompute")
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -106,7 +106,7 @@ def main():
     Q, K, V, dO = tens["Q"], tens["K"], tens["V"], tens["dO"]
     q2k_d = torch.from_numpy(q2k).to(dev)
     scale = 1.0 / math.sqrt(128.0)
-    mode = M.DQ_ACCUM_FP32 if args.dq_mode == "fp32" else M.DQ_ACCUM_BF16X2
+    mode = {"recompute": M.DQ_RECOMPUTE, "fp32": M.DQ_ACCUM_FP32, "bf16x2": M.DQ_ACCUM_BF16X2}[args.dq_mode]
     m = M.MSA(cu, grid=args.grid or None, dq_mode=mode, device=dev)
     O = torch.empty_like(Q)
     LSE = torch.empty((T, 64), dtype=torch.float32, device=dev)

@@ -17,8 +17,9 @@ import numpy as np
 from .build import LIB as _LIB_PATH
 
 NUM_Q_HEADS, NUM_KV_HEADS, NUM_INDEX_HEADS, HEAD_DIM, BLOCK, TOPK = 64, 4, 4, 128, 128, 16
-TILE_QUERIES, FWD_GROUP = 8, 16
-DQ_ACCUM_FP32, DQ_ACCUM_BF16X2 = 0, 1
+PLAN_MAX_LIST = 8 * 16
+TILE_QUERIES, FWD_GROUP = 8, 8
+DQ_ACCUM_FP32, DQ_ACCUM_BF16X2, DQ_RECOMPUTE = 0, 1, 2
 Q2K_OUT_OF_RANGE, Q2K_DUPLICATE = 1, 2
 PLAN_HEADER_WORDS, TASKS_HEADER_WORDS = 16, 64
 
@@ -65,14 +66,14 @@ def lib():
             "msa_tasks_bytes": (Z, [LP, I]),
             "msa_bwd_scratch_bytes": (Z, [LP, I]),
             "msa_default_grid": (I, []),
-            "msa_align_kv": (I, [P, P, LP, P, P, P]),
+            "msa_align_kv": (I, [P, P, LP, P, P, P, P, P]),
             "msa_build_k2q_csr": (I, [P, LP, P, P, P, P, Z, P]),
             "msa_plan": (I, [LP, P, P, Z, P]),
             "msa_forward": (I, [P, P, P, P, LP, P, F, P, P, P]),
             "msa_backward_preprocess": (I, [P, P, I, P, P]),
             "msa_tasks_meta_offset": (Z, [I]),
             "msa_build_tasks": (I, [LP, P, P, I, P, Z, P]),
-            "msa_backward": (I, [P, P, P, P, P, P, P, I, LP, F, I, P, P, P, P, Z, P]),
+            "msa_backward": (I, [P, P, P, P, P, P, P, P, P, P, I, LP, F, I, P, P, P, P, Z, P]),
             "msa_status_string": (ctypes.c_char_p, [I]),
             "msa_set_backward_timing_events": (None, [P, P]),
         }
@@ -156,9 +157,9 @@ def msa_tasks_meta_offset(grid):
     return lib().msa_tasks_meta_offset(grid)
 
 
-def msa_align_kv(K, V, layout, Kw, Vw, stream=None):
+def msa_align_kv(K, V, layout, Kw, Vw, Kt, Vt, stream=None):
     _check("msa_align_kv", lib().msa_align_kv(_ptr(K), _ptr(V), layout.ref(), _ptr(Kw), _ptr(Vw),
-                                              _stream(stream)))
+                                              _ptr(Kt), _ptr(Vt), _stream(stream)))
 
 
 def msa_build_k2q_csr(q2k, layout, row_ptr, cols, status, scratch, stream=None):
@@ -172,8 +173,8 @@ def msa_plan(layout, q2k, plan, stream=None):
                                       plan.numel() * plan.element_size(), _stream(stream)))
 
 
-def msa_forward(Q, Kw, Vw, q2k, layout, plan, scale, O, LSE, stream=None):
-    _check("msa_forward", lib().msa_forward(_ptr(Q), _ptr(Kw), _ptr(Vw), _ptr(q2k), layout.ref(),
+def msa_forward(Q, Kw, Vt, q2k, layout, plan, scale, O, LSE, stream=None):
+    _check("msa_forward", lib().msa_forward(_ptr(Q), _ptr(Kw), _ptr(Vt), _ptr(q2k), layout.ref(),
                                             _ptr(plan), float(scale), _ptr(O), _ptr(LSE),
                                             _stream(stream)))
 
@@ -189,10 +190,11 @@ def msa_build_tasks(layout, row_ptr, cols, grid, tasks, stream=None):
                                                     _stream(stream)))
 
 
-def msa_backward(Q, Kw, Vw, dO, LSE, delta, tasks, grid, layout, scale, mode, dQ, dK, dV, scratch,
-                 stream=None):
+def msa_backward(Q, Kw, Vw, Kt, dO, LSE, delta, q2k, plan, tasks, grid, layout, scale, mode, dQ, dK,
+                 dV, scratch, stream=None):
     _check("msa_backward", lib().msa_backward(
-        _ptr(Q), _ptr(Kw), _ptr(Vw), _ptr(dO), _ptr(LSE), _ptr(delta), _ptr(tasks), int(grid),
+        _ptr(Q), _ptr(Kw), _ptr(Vw), _ptr(Kt), _ptr(dO), _ptr(LSE), _ptr(delta), _ptr(q2k),
+        _ptr(plan), _ptr(tasks), int(grid),
         layout.ref(), float(scale), int(mode), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(scratch),
         scratch.numel() * scratch.element_size(), _stream(stream)))
 
@@ -212,11 +214,12 @@ def _bytes(n, device):
 class MSA:
     """Buffers of one layout plus the forward and backward call sequences."""
 
-    def __init__(self, cu_seqlens, grid=None, dq_mode=DQ_ACCUM_FP32, device="cuda"):
+    def __init__(self, cu_seqlens, grid=None, dq_mode=DQ_RECOMPUTE, device="cuda"):
         import torch
         self.layout = L = Layout(cu_seqlens, device)
         self.device = device
         self.grid = int(grid) if grid else msa_default_grid()
+        self.fwd_group = FWD_GROUP
         self.dq_mode = dq_mode
         self.row_ptr = torch.empty(NUM_INDEX_HEADS * L.NB + 1, dtype=torch.int32, device=device)
         self.cols = torch.empty(msa_csr_cols_capacity(L), dtype=torch.int32, device=device)
@@ -227,6 +230,8 @@ class MSA:
         self.bwd_scratch = _bytes(msa_bwd_scratch_bytes(L, dq_mode), device)
         self.Kw = torch.empty((L.W, NUM_KV_HEADS, HEAD_DIM), dtype=torch.bfloat16, device=device)
         self.Vw = torch.empty_like(self.Kw)
+        self.Kt = torch.empty_like(self.Kw)  # [4][W/128][128][128] transposed blocks
+        self.Vt = torch.empty_like(self.Kw)
         self.delta = torch.empty((L.T, NUM_Q_HEADS), dtype=torch.float32, device=device)
 
     def forward(self, Q, K, V, q2k, scale, O=None, LSE=None, stream=None):
@@ -239,13 +244,14 @@ class MSA:
             LSE = torch.empty((L.T, NUM_Q_HEADS), dtype=torch.float32, device=self.device)
         msa_build_k2q_csr(q2k, L, self.row_ptr, self.cols, self.status, self.csr_scratch, stream)
         msa_plan(L, q2k, self.plan, stream)
-        msa_align_kv(K, V, L, self.Kw, self.Vw, stream)
-        msa_forward(Q, self.Kw, self.Vw, q2k, L, self.plan, scale, O, LSE, stream)
+        msa_align_kv(K, V, L, self.Kw, self.Vw, self.Kt, self.Vt, stream)
+        msa_forward(Q, self.Kw, self.Vt, q2k, L, self.plan, scale, O, LSE, stream)
+        self.q2k = q2k
         return O, LSE
 
     def backward(self, Q, dO, O, LSE, scale, dQ=None, dK=None, dV=None, stream=None):
-        """Preprocess + task tables + backward (uses the CSR and K/V workspace of the
-        last forward).  Returns (dQ, dK, dV) in compact order."""
+        """Preprocess + task tables + backward (uses the CSR, plan, q2k and K/V workspace
+        of the last forward).  Returns (dQ, dK, dV) in compact order."""
         import torch
         L = self.layout
         if dQ is None:
@@ -256,8 +262,9 @@ class MSA:
             dV = torch.empty_like(dK)
         msa_backward_preprocess(O, dO, L.T, self.delta, stream)
         msa_build_tasks(L, self.row_ptr, self.cols, self.grid, self.tasks, stream)
-        msa_backward(Q, self.Kw, self.Vw, dO, LSE, self.delta, self.tasks, self.grid, L, scale,
-                     self.dq_mode, dQ, dK, dV, self.bwd_scratch, stream)
+        msa_backward(Q, self.Kw, self.Vw, self.Kt, dO, LSE, self.delta, self.q2k, self.plan,
+                     self.tasks, self.grid, L, scale, self.dq_mode, dQ, dK, dV, self.bwd_scratch,
+                     stream)
         return dQ, dK, dV
 
     # ---- views of the integer structures (for checks)
@@ -266,8 +273,17 @@ class MSA:
         return rp, self.cols[: int(rp[-1])].cpu().numpy()
 
     def plan_items(self):
+        """(items int32 [n, 4] = {i, t0, n, doc}, walk lists [(block, mask)] per item)."""
+        L = self.layout
         w = self.plan.view(torch_int32()).cpu().numpy()
-        return w[PLAN_HEADER_WORDS: PLAN_HEADER_WORDS + 4 * int(w[0])].reshape(-1, 4)
+        ni = 4 * ((L.T + FWD_GROUP - 1) // FWD_GROUP + L.num_docs)
+        n = int(w[0])
+        items = w[PLAN_HEADER_WORDS: PLAN_HEADER_WORDS + 4 * n].reshape(-1, 4)
+        lens = w[PLAN_HEADER_WORDS + 4 * ni: PLAN_HEADER_WORDS + 4 * ni + n]
+        base = PLAN_HEADER_WORDS + 4 * ni + (ni + 3) // 4 * 4
+        lists = [w[base + 2 * PLAN_MAX_LIST * p: base + 2 * PLAN_MAX_LIST * p + 2 * int(lens[p])].reshape(-1, 2)
+                 for p in range(n)]
+        return items, lists
 
     def task_tables(self):
         w = self.tasks.view(torch_int32()).cpu().numpy()

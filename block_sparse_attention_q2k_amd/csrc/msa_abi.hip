@@ -113,8 +113,13 @@ size_t msa_tasks_meta_offset(int32_t grid) {
 size_t msa_bwd_scratch_bytes(const msa_layout *layout, int dq_accum_mode) {
   LayoutArgs L;
   if (check_layout(layout, &L)) return 0;
-  if (dq_accum_mode != MSA_DQ_ACCUM_FP32 && dq_accum_mode != MSA_DQ_ACCUM_BF16X2) return 0;
-  size_t elem = dq_accum_mode == MSA_DQ_ACCUM_FP32 ? 4 : 2;
+  size_t elem;
+  switch (dq_accum_mode) {
+    case MSA_DQ_ACCUM_FP32: elem = 4; break;
+    case MSA_DQ_ACCUM_BF16X2: elem = 2; break;
+    case MSA_DQ_RECOMPUTE: elem = 0; break;
+    default: return 0;
+  }
   size_t dq = round16((size_t)L.T * MSA_NUM_Q_HEADS * MSA_HEAD_DIM * elem);
   size_t kv = round16((size_t)L.W * MSA_NUM_KV_HEADS * MSA_HEAD_DIM * 4);
   return dq + 2 * kv;
@@ -129,13 +134,13 @@ int32_t msa_default_grid(void) {
 }
 
 int msa_align_kv(const msa_bf16 *K, const msa_bf16 *V, const msa_layout *layout, msa_bf16 *Kw,
-                 msa_bf16 *Vw, void *stream) {
+                 msa_bf16 *Vw, msa_bf16 *Kt, msa_bf16 *Vt, void *stream) {
   LayoutArgs L;
   int rc = check_layout(layout, &L);
-  if (!rc) rc = check_ptrs({K, V, Kw, Vw});
+  if (!rc) rc = check_ptrs({K, V, Kw, Vw, Kt, Vt});
   if (!rc) rc = check_device();
   if (rc) return rc;
-  return launch_rc(host::align_kv(K, V, L, Kw, Vw, (hipStream_t)stream));
+  return launch_rc(host::align_kv(K, V, L, Kw, Vw, Kt, Vt, (hipStream_t)stream));
 }
 
 int msa_build_k2q_csr(const int32_t *q2k, const msa_layout *layout, int32_t *row_ptr,
@@ -162,16 +167,16 @@ int msa_plan(const msa_layout *layout, const int32_t *q2k, void *plan, size_t pl
   return launch_rc(host::build_plan(L, q2k, plan, (hipStream_t)stream));
 }
 
-int msa_forward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, const int32_t *q2k,
+int msa_forward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vt, const int32_t *q2k,
                 const msa_layout *layout, const void *plan, float scale, msa_bf16 *O,
                 float *LSE, void *stream) {
   LayoutArgs L;
   int rc = check_layout(layout, &L);
-  if (!rc) rc = check_ptrs({Q, Kw, Vw, q2k, plan, O, LSE});
+  if (!rc) rc = check_ptrs({Q, Kw, Vt, q2k, plan, O, LSE});
   if (rc) return rc;
   if (!(scale > 0.f) || scale != scale) return MSA_ERR_SHAPE;
   if ((rc = check_device())) return rc;
-  return launch_rc(host::forward(Q, Kw, Vw, q2k, L, plan, scale, O, LSE, (hipStream_t)stream));
+  return launch_rc(host::forward(Q, Kw, Vt, q2k, L, plan, scale, O, LSE, (hipStream_t)stream));
 }
 
 int msa_backward_preprocess(const msa_bf16 *O, const msa_bf16 *dO, int32_t num_tokens,
@@ -195,22 +200,25 @@ int msa_build_tasks(const msa_layout *layout, const int32_t *row_ptr, const int3
   return launch_rc(host::build_tasks(L, row_ptr, cols, grid, tasks, (hipStream_t)stream));
 }
 
-int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, const msa_bf16 *dO,
-                 const float *LSE, const float *delta, const void *tasks, int32_t grid,
-                 const msa_layout *layout, float scale, int dq_accum_mode, msa_bf16 *dQ,
-                 msa_bf16 *dK, msa_bf16 *dV, void *scratch, size_t scratch_bytes,
-                 void *stream) {
+int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, const msa_bf16 *Kt,
+                 const msa_bf16 *dO, const float *LSE, const float *delta, const int32_t *q2k,
+                 const void *plan, const void *tasks, int32_t grid, const msa_layout *layout,
+                 float scale, int dq_accum_mode, msa_bf16 *dQ, msa_bf16 *dK, msa_bf16 *dV,
+                 void *scratch, size_t scratch_bytes, void *stream) {
   LayoutArgs L;
   int rc = check_layout(layout, &L);
-  if (!rc) rc = check_ptrs({Q, Kw, Vw, dO, LSE, delta, tasks, dQ, dK, dV, scratch});
+  if (!rc) rc = check_ptrs({Q, Kw, Vw, Kt, dO, LSE, delta, q2k, plan, tasks, dQ, dK, dV, scratch});
   if (rc) return rc;
   if (grid < 1 || grid > MSA_MAX_GRID) return MSA_ERR_GRID;
-  if (dq_accum_mode != MSA_DQ_ACCUM_FP32 && dq_accum_mode != MSA_DQ_ACCUM_BF16X2) return MSA_ERR_MODE;
+  if (dq_accum_mode != MSA_DQ_ACCUM_FP32 && dq_accum_mode != MSA_DQ_ACCUM_BF16X2 &&
+      dq_accum_mode != MSA_DQ_RECOMPUTE)
+    return MSA_ERR_MODE;
   if (!(scale > 0.f) || scale != scale) return MSA_ERR_SHAPE;
   if (scratch_bytes < msa_bwd_scratch_bytes(layout, dq_accum_mode)) return MSA_ERR_SCRATCH;
   if ((rc = check_device())) return rc;
   hipStream_t s = (hipStream_t)stream;
-  size_t elem = dq_accum_mode == MSA_DQ_ACCUM_FP32 ? 4 : 2;
+  const bool pool = dq_accum_mode != MSA_DQ_RECOMPUTE;
+  size_t elem = dq_accum_mode == MSA_DQ_ACCUM_FP32 ? 4 : (pool ? 2 : 0);
   size_t dq_bytes = round16((size_t)L.T * MSA_NUM_Q_HEADS * MSA_HEAD_DIM * elem);
   size_t kv_bytes = round16((size_t)L.W * MSA_NUM_KV_HEADS * MSA_HEAD_DIM * 4);
   char *sc = (char *)scratch;
@@ -219,11 +227,18 @@ int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, cons
   hipError_t e = host::fill_u32(sc, (dq_bytes + 2 * kv_bytes) / 4, 0u, s);
   const bool timed = t_bwd_start && t_bwd_stop;
   if (e == hipSuccess && timed) e = hipEventRecord(t_bwd_start, s);
-  if (e == hipSuccess)
-    e = host::backward_main(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dq_accum_mode, sc,
-                            dk_pool, dv_pool, s);
+  if (e == hipSuccess) {
+    if (pool)
+      e = host::backward_main(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dq_accum_mode, sc,
+                              dk_pool, dv_pool, s);
+    else
+      e = host::backward_kv(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dk_pool, dv_pool, s);
+  }
   if (e == hipSuccess && timed) e = hipEventRecord(t_bwd_stop, s);
-  if (e == hipSuccess) e = host::finalize(sc, dq_accum_mode, dk_pool, dv_pool, L, dQ, dK, dV, s);
+  if (e == hipSuccess && !pool)
+    e = host::backward_dq(Q, dO, Kw, Vw, Kt, LSE, delta, q2k, L, plan, scale, dQ, s);
+  if (e == hipSuccess)
+    e = host::finalize(pool ? sc : nullptr, dq_accum_mode, dk_pool, dv_pool, L, dQ, dK, dV, s);
   return launch_rc(e);
 }
 

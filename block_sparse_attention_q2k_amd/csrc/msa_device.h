@@ -18,6 +18,7 @@ constexpr int kTileQ = MSA_TILE_QUERIES;    // 8 queries per backward task row
 constexpr int kFwdGroup = MSA_FWD_GROUP;    // queries per forward work item
 constexpr int kTasksHeaderWords = 64;
 constexpr int kPlanHeaderWords = 16;
+constexpr int kPlanMaxList = kFwdGroup * kTopk;  // walk-list capacity per plan item
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

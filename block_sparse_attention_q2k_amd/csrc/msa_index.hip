@@ -41,6 +41,36 @@ __global__ void align_kv_kernel(const u32x4 *__restrict__ K, const u32x4 *__rest
   Vw[gid] = v;
 }
 
+// Transposed per-block copies of the workspace: Xt[kv][gb][dim][key] =
+// Xw[gb * 128 + key][kv][dim] (keys contiguous), the MFMA A operand of V^T P^T and
+// K^T dS^T.  One workgroup per (block, KV head, tensor).
+__global__ void __launch_bounds__(256)
+transpose_blocks_kernel(const uint16_t *__restrict__ Kw, const uint16_t *__restrict__ Vw, int NB,
+                        uint16_t *__restrict__ Kt, uint16_t *__restrict__ Vt) {
+  __shared__ uint32_t tile[128 * 65];  // 128 keys x 128 dims bf16, rows padded to 260 B
+  const int gb = blockIdx.x, kv = blockIdx.y, tid = threadIdx.x;
+  const uint16_t *X = blockIdx.z ? Vw : Kw;
+  uint16_t *Y = blockIdx.z ? Vt : Kt;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int id = tid + 256 * k, key = id >> 4, c = id & 15;
+    const u32x4 v = *(const u32x4 *)(X + ((size_t)(gb * kBlk + key) * kHKV + kv) * kD + c * 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tile[key * 65 + 4 * c + q] = v[q];
+  }
+  __syncthreads();
+  const uint16_t *t16 = (const uint16_t *)tile;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int id = tid + 256 * k, dim = id >> 4, c = id & 15;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = (uint32_t)t16[(8 * c + 2 * q) * 130 + dim] | ((uint32_t)t16[(8 * c + 2 * q + 1) * 130 + dim] << 16);
+    *(u32x4 *)(Y + (((size_t)kv * NB + gb) * kD + dim) * kBlk + c * 8) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
 // ------------------------------------------------------------------ q2k membership
 // Member blocks of one (index head, query) row: ids in [0, blk_t], first listing only.
 // Returns a 16-bit mask of member slots and ORs precondition flags into *flags.
@@ -70,33 +100,72 @@ __device__ inline uint32_t member_mask(const int32_t *__restrict__ row, int blk_
   return m;
 }
 
-// CSR count (pass 0) and fill (pass 1): one thread per (index head, query).
+// CSR count (pass 0) and fill (pass 1).  Workgroup (chunk, i) handles 256 consecutive
+// queries of index head i.  Its rows i * NB + [gb_lo, gb_hi] span at most the blocks of
+// the documents it touches; when that span fits in LDS the workgroup first counts per
+// row in LDS and issues one global atomic per touched row (the sink and diagonal rows
+// are hit by every query of a document), else every slot goes to global memory.
+constexpr int kCsrSpan = 4096;
 template <int kPass>
-__global__ void csr_kernel(const int32_t *__restrict__ q2k, const int32_t *__restrict__ cu,
-                           const int32_t *__restrict__ cu_ws, int ndocs, int T, int NB,
-                           int32_t *__restrict__ counter, int32_t *__restrict__ cols,
-                           int32_t *__restrict__ status) {
-  int gid = blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= kHI * T) return;
-  int i = gid / T, t = gid - i * T;
-  int d = upper_index(cu, ndocs - 1, t);
-  int pos = t - cu[d];
-  int gb0 = cu_ws[d] / kBlk;
+__global__ void __launch_bounds__(256)
+csr_kernel(const int32_t *__restrict__ q2k, const int32_t *__restrict__ cu,
+           const int32_t *__restrict__ cu_ws, int ndocs, int T, int NB,
+           int32_t *__restrict__ counter, int32_t *__restrict__ cols, int32_t *__restrict__ status) {
+  __shared__ int32_t hist[kCsrSpan];
+  __shared__ int32_t base[kPass == 1 ? kCsrSpan : 1];
+  const int i = blockIdx.y, tid = threadIdx.x;
+  const int t_first = blockIdx.x * 256, t_last = min(T, t_first + 256) - 1;
+  const int t = t_first + tid;
+  const bool active = t <= t_last;
+  int d = 0, pos = 0;
+  if (active) {
+    d = upper_index(cu, ndocs - 1, t);
+    pos = t - cu[d];
+  }
+  const int d0 = upper_index(cu, ndocs - 1, t_first), d1 = upper_index(cu, ndocs - 1, t_last);
+  const int gb_lo = cu_ws[d0] / kBlk;
+  const int gb_hi = (cu_ws[d1] + (t_last - cu[d1])) / kBlk;
+  const int span = gb_hi - gb_lo + 1;
+  const bool local = span <= kCsrSpan;
   int32_t ids[kTopk];
+  uint32_t m = 0;
   int flags = 0;
-  uint32_t m = member_mask(q2k + (size_t)gid * kTopk, pos / kBlk, ids, &flags);
+  if (active) m = member_mask(q2k + ((size_t)i * T + t) * kTopk, pos / kBlk, ids, &flags);
   if (kPass == 0 && flags) atomicOr(status, flags);
-  int rbase = i * NB + gb0;
+  const int gb0 = active ? cu_ws[d] / kBlk : 0;
+  const int rbase = i * NB;
+  if (!local) {
+#pragma unroll
+    for (int j = 0; j < kTopk; ++j) {
+      if (!((m >> j) & 1)) continue;
+      const int r = rbase + gb0 + ids[j];
+      if (kPass == 0) atomicAdd(&counter[r], 1);
+      else cols[atomicAdd(&counter[r], 1)] = t;
+    }
+    return;
+  }
+  for (int k = tid; k < span; k += 256) hist[k] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kTopk; ++j)
+    if ((m >> j) & 1) atomicAdd(&hist[gb0 + ids[j] - gb_lo], 1);
+  __syncthreads();
+  for (int k = tid; k < span; k += 256) {
+    const int c = hist[k];
+    if (kPass == 0) {
+      if (c) atomicAdd(&counter[rbase + gb_lo + k], c);
+    } else {
+      base[k] = c ? atomicAdd(&counter[rbase + gb_lo + k], c) : 0;
+      hist[k] = 0;
+    }
+  }
+  if (kPass == 0) return;
+  __syncthreads();
 #pragma unroll
   for (int j = 0; j < kTopk; ++j) {
     if (!((m >> j) & 1)) continue;
-    int r = rbase + ids[j];
-    if (kPass == 0) {
-      atomicAdd(&counter[r], 1);
-    } else {
-      int slot = atomicAdd(&counter[r], 1);
-      cols[slot] = t;
-    }
+    const int k = gb0 + ids[j] - gb_lo;
+    cols[base[k] + atomicAdd(&hist[k], 1)] = t;
   }
 }
 
@@ -137,9 +206,74 @@ __global__ void row_len_kernel(const int32_t *__restrict__ row_ptr, int n, int32
 }
 
 // ------------------------------------------------------------------ forward plan
-// plan layout (int32): [0] items, [1] groups per head G, [2] Gmax; items at
-// [16 + 4p]; aux: gstart [ndocs+1] at aux0, group info {t0,n,d,_} x Gmax at aux1,
-// cost [4 x Gmax] at aux2.
+// plan layout (int32): [0] items, [1] groups per head G, [2] Gmax; items {i, t0, n, doc}
+// at [16 + 4p]; walk-list lengths at PlanView::len; walk lists (block, unit mask) at
+// PlanView::lists + 2 * kPlanMaxList * p; aux: gstart [ndocs+1], group info {t0,n,d,_}
+// x Gmax, cost [4 x Gmax].
+
+// Walk list of one item (one wave per item): its queries' member blocks in ascending
+// order with the mask of queries selecting each.  The <= 128 (block, query) keys are
+// bitonic-sorted in LDS; the first key of each block run emits (block, OR of run).
+__global__ void __launch_bounds__(64)
+plan_lists_kernel(const int32_t *__restrict__ q2k, const int32_t *__restrict__ cu, int T,
+                  const int32_t *__restrict__ plan, int32_t *__restrict__ len,
+                  int32_t *__restrict__ lists) {
+  __shared__ int32_t keys[kPlanMaxList];
+  const int p = blockIdx.x, lane = threadIdx.x;
+  if (p >= plan[0]) return;
+  const i32x4 it = ((const i32x4 *)(plan + kPlanHeaderWords))[p];
+  const int i = it[0], t0 = it[1], n = it[2], d = it[3];
+  const int p0 = t0 - cu[d];
+  constexpr int kNone = 0x7fffffff;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = lane + 64 * h, u = e >> 4, j = e & 15;
+    int key = kNone;
+    if (u < n) {
+      const int b = q2k[((size_t)i * T + t0 + u) * kTopk + j];
+      if (b >= 0 && b <= (p0 + u) / kBlk) key = (b << 4) | u;
+    }
+    keys[e] = key;
+  }
+  __syncthreads();
+  for (int k = 2; k <= kPlanMaxList; k <<= 1)
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      const int a = (lane / jj) * 2 * jj + (lane % jj), b = a + jj;  // one pair per lane
+      const int ka = keys[a], kb = keys[b];
+      const bool up = (a & k) == 0;
+      if ((ka > kb) == up) {
+        keys[a] = kb;
+        keys[b] = ka;
+      }
+      __syncthreads();
+    }
+  int start[2], mask[2], blk[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = lane + 64 * h, k = keys[e];
+    blk[h] = k >> 4;
+    start[h] = k != kNone && (e == 0 || (keys[e - 1] >> 4) != blk[h]);
+    mask[h] = 0;
+    if (start[h])
+      for (int f = e; f < kPlanMaxList && keys[f] != kNone && (keys[f] >> 4) == blk[h]; ++f)
+        mask[h] |= 1 << (keys[f] & 15);
+  }
+  const uint64_t b0 = __ballot(start[0]), b1 = __ballot(start[1]);
+  const uint64_t below = (1ull << lane) - 1;
+  int32_t *out = lists + (size_t)2 * kPlanMaxList * p;
+  if (start[0]) {
+    const int r = __popcll(b0 & below);
+    out[2 * r] = blk[0];
+    out[2 * r + 1] = mask[0];
+  }
+  if (start[1]) {
+    const int r = __popcll(b0) + __popcll(b1 & below);
+    out[2 * r] = blk[1];
+    out[2 * r + 1] = mask[1];
+  }
+  if (lane == 0) len[p] = __popcll(b0) + __popcll(b1);
+}
+
 __global__ void __launch_bounds__(1024)
 plan_groups_kernel(const int32_t *__restrict__ cu, int ndocs, int Gmax, int32_t *__restrict__ plan,
                    int32_t *__restrict__ gstart) {
@@ -371,10 +505,12 @@ hipError_t fill_u32(void *p, size_t n, uint32_t v, hipStream_t s) {
 }
 
 hipError_t align_kv(const void *K, const void *V, const LayoutArgs &L, void *Kw, void *Vw,
-                    hipStream_t s) {
+                    void *Kt, void *Vt, hipStream_t s) {
   size_t n = (size_t)L.W * 64;
   hipLaunchKernelGGL(align_kv_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s, (const u32x4 *)K,
                      (const u32x4 *)V, L.cu, L.cu_ws, L.ndocs, L.W, (u32x4 *)Kw, (u32x4 *)Vw);
+  hipLaunchKernelGGL(transpose_blocks_kernel, dim3(L.NB, kHKV, 2), dim3(256), 0, s,
+                     (const uint16_t *)Kw, (const uint16_t *)Vw, L.NB, (uint16_t *)Kt, (uint16_t *)Vt);
   return hipGetLastError();
 }
 
@@ -385,36 +521,48 @@ hipError_t build_csr(const int32_t *q2k, const LayoutArgs &L, int32_t *row_ptr, 
   if (e != hipSuccess) return e;
   e = fill_u32(status, 1, 0, s);
   if (e != hipSuccess) return e;
-  unsigned nb = blocks_for((size_t)kHI * L.T, 256);
-  hipLaunchKernelGGL(csr_kernel<0>, dim3(nb), dim3(256), 0, s, q2k, L.cu, L.cu_ws, L.ndocs, L.T,
-                     L.NB, counter, cols, status);
+  const dim3 g(blocks_for((size_t)L.T, 256), kHI);
+  hipLaunchKernelGGL(csr_kernel<0>, g, dim3(256), 0, s, q2k, L.cu, L.cu_ws, L.ndocs, L.T, L.NB,
+                     counter, cols, status);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, counter, nrows, 0, row_ptr, counter);
-  hipLaunchKernelGGL(csr_kernel<1>, dim3(nb), dim3(256), 0, s, q2k, L.cu, L.cu_ws, L.ndocs, L.T,
-                     L.NB, counter, cols, status);
+  hipLaunchKernelGGL(csr_kernel<1>, g, dim3(256), 0, s, q2k, L.cu, L.cu_ws, L.ndocs, L.T, L.NB,
+                     counter, cols, status);
   return hipGetLastError();
 }
 
 size_t plan_gmax(const LayoutArgs &L) { return (size_t)(L.T + kFwdGroup - 1) / kFwdGroup + L.ndocs; }
 
+PlanView plan_view(const LayoutArgs &L, void *plan_v) {
+  PlanView v;
+  int32_t *plan = (int32_t *)plan_v;
+  const size_t gmax = plan_gmax(L), nitems = kHI * gmax;
+  v.header = plan;
+  v.items = plan + kPlanHeaderWords;
+  v.len = v.items + 4 * nitems;
+  v.lists = v.len + (nitems + 3) / 4 * 4;
+  v.gstart = v.lists + 2 * kPlanMaxList * nitems;
+  v.ginfo = v.gstart + ((L.ndocs + 1 + 3) / 4) * 4;
+  v.cost = v.ginfo + 4 * gmax;
+  v.end = v.cost + kHI * gmax;
+  return v;
+}
+
 size_t plan_bytes(const LayoutArgs &L) {
-  size_t gmax = plan_gmax(L);
-  size_t words = kPlanHeaderWords + 4 * kHI * gmax  // items
-                 + ((L.ndocs + 1 + 3) / 4) * 4      // gstart
-                 + 4 * gmax                         // group info
-                 + kHI * gmax;                      // cost
-  return words * 4;
+  PlanView v = plan_view(L, nullptr);
+  return (size_t)(v.end - v.header) * 4;
 }
 
 hipError_t build_plan(const LayoutArgs &L, const int32_t *q2k, void *plan_v, hipStream_t s) {
-  int32_t *plan = (int32_t *)plan_v;
-  int gmax = (int)plan_gmax(L);
-  int32_t *gstart = plan + kPlanHeaderWords + 4 * kHI * gmax;
-  i32x4 *ginfo = (i32x4 *)(gstart + ((L.ndocs + 1 + 3) / 4) * 4);
-  int32_t *cost = (int32_t *)(ginfo + gmax);
-  hipLaunchKernelGGL(plan_groups_kernel, dim3(1), dim3(1024), 0, s, L.cu, L.ndocs, gmax, plan, gstart);
+  PlanView v = plan_view(L, plan_v);
+  const int gmax = (int)plan_gmax(L);
+  hipLaunchKernelGGL(plan_groups_kernel, dim3(1), dim3(1024), 0, s, L.cu, L.ndocs, gmax, v.header,
+                     v.gstart);
   hipLaunchKernelGGL(plan_cost_kernel, dim3(blocks_for((size_t)kHI * gmax, 128)), dim3(128), 0, s,
-                     q2k, L.cu, L.ndocs, L.T, gmax, plan, gstart, ginfo, cost);
-  hipLaunchKernelGGL(plan_sort_kernel, dim3(kHI), dim3(1024), 0, s, gmax, plan, ginfo, cost);
+                     q2k, L.cu, L.ndocs, L.T, gmax, v.header, v.gstart, (i32x4 *)v.ginfo, v.cost);
+  hipLaunchKernelGGL(plan_sort_kernel, dim3(kHI), dim3(1024), 0, s, gmax, v.header,
+                     (const i32x4 *)v.ginfo, v.cost);
+  hipLaunchKernelGGL(plan_lists_kernel, dim3(kHI * gmax), dim3(64), 0, s, q2k, L.cu, L.T, v.header,
+                     v.len, v.lists);
   return hipGetLastError();
 }
 
@@ -473,7 +621,7 @@ hipError_t preprocess(const void *O, const void *dO, int T, float *delta, hipStr
 
 hipError_t finalize(const void *dq_pool, int mode, const float *dk_pool, const float *dv_pool,
                     const LayoutArgs &L, void *dQ, void *dK, void *dV, hipStream_t s) {
-  size_t dq_chunks = (size_t)L.T * kH * kD / 8;
+  size_t dq_chunks = dq_pool ? (size_t)L.T * kH * kD / 8 : 0;  // no pool: dQ already final
   size_t kv_chunks = (size_t)L.T * kHKV * kD / 8;
   hipLaunchKernelGGL(finalize_kernel, dim3(blocks_for(dq_chunks + kv_chunks, 256)), dim3(256), 0, s,
                      dq_pool, mode, dq_chunks, dk_pool, dv_pool, L.cu, L.cu_ws, L.ndocs, L.T,

@@ -46,7 +46,7 @@ extern "C" {
  * module summary). */
 #define MSA_TILE_QUERIES 8
 /* Forward work item: up to this many consecutive queries of one document. */
-#define MSA_FWD_GROUP 16
+#define MSA_FWD_GROUP 8
 
 typedef uint16_t msa_bf16;
 
@@ -68,9 +68,14 @@ enum {
   MSA_Q2K_DUPLICATE = 2     /* an id listed twice for one (index head, query) (ignored) */
 };
 
-/* dQ accumulation pool of msa_backward (pull-request page, Supported scope: dQ takes
- * 16-bit atomic accumulation, dK/dV FP32). */
-enum { MSA_DQ_ACCUM_FP32 = 0, MSA_DQ_ACCUM_BF16X2 = 1 };
+/* How msa_backward forms dQ.  The pages accumulate dQ with 16-bit atomics into a pool
+ * (pull-request page, Supported scope; msa_backward_sm100 API page, module summary):
+ * modes FP32 and BF16X2 do that (fp32 atomics / packed bf16 pair atomics from the
+ * KV-parallel kernel, then a cast).  MSA_DQ_RECOMPUTE instead computes dQ in a
+ * query-parallel kernel that recomputes P and dS per selected block and stores dQ
+ * directly (no pool, no atomics); it is the fastest on gfx950, where global atomic
+ * throughput, not the matrix cores, bounds the pooled modes. */
+enum { MSA_DQ_ACCUM_FP32 = 0, MSA_DQ_ACCUM_BF16X2 = 1, MSA_DQ_RECOMPUTE = 2 };
 
 #define MSA_MAX_GRID 4096
 
@@ -108,7 +113,7 @@ size_t msa_csr_cols_capacity(const msa_layout *layout);
 size_t msa_plan_bytes(const msa_layout *layout);
 /* Bytes of the backward task buffer for a grid of `grid` workgroups. */
 size_t msa_tasks_bytes(const msa_layout *layout, int32_t grid);
-/* Bytes of the backward scratch (dQ pool in `dq_accum_mode`, fp32 dK/dV pools). */
+/* Bytes of the backward scratch (dQ pool of `dq_accum_mode`, if any; fp32 dK/dV pools). */
 size_t msa_bwd_scratch_bytes(const msa_layout *layout, int dq_accum_mode);
 /* Grid size msa_build_tasks / msa_backward use by default (one workgroup per CU). */
 int32_t msa_default_grid(void);
@@ -118,10 +123,11 @@ int32_t msa_default_grid(void);
  * document padded to a multiple of 128 tokens; msa_backward_sm100 API page,
  * run_backward: W a positive multiple of 128).
  *   K, V: bf16 [T, 4, 128] compact.  Kw, Vw: bf16 [W, 4, 128]; row cu_ws[d] + p holds
- *   compact row cu[d] + p for p < L_d and zeros after.
+ *   compact row cu[d] + p for p < L_d and zeros after.  Kt, Vt: bf16 [4][W/128][128]
+ *   [128], the same blocks transposed: Kt[kv][gb][c][k] = Kw[128 gb + k][kv][c].
  * --------------------------------------------------------------------------------- */
 int msa_align_kv(const msa_bf16 *K, const msa_bf16 *V, const msa_layout *layout,
-                 msa_bf16 *Kw, msa_bf16 *Vw, void *stream);
+                 msa_bf16 *Kw, msa_bf16 *Vw, msa_bf16 *Kt, msa_bf16 *Vt, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * q2k -> k2q CSR inversion (pull-request page, Design: forward-derived CSR; bindings
@@ -143,19 +149,26 @@ int msa_build_k2q_csr(const int32_t *q2k, const msa_layout *layout, int32_t *row
  * document into groups of MSA_FWD_GROUP consecutive queries; each (index head, group)
  * is one work item.  Items of one head are ordered by cost (member slots) descending,
  * ties in document order, and heads are interleaved: item p belongs to head p % 4.
- * Layout of `plan` (int32): plan[0] = item count; items at plan[16 + 4p] = {i, t0, n,
- * doc}.  q2k as above.
+ * Each item carries its walk list: the member blocks of its queries in ascending order,
+ * each with the bit mask of the item's queries (bit u = query t0 + u) that select it;
+ * msa_forward and the dQ step of msa_backward walk these lists.
+ * Layout of `plan` (int32 words; NI = 4 * (ceil(T / MSA_FWD_GROUP) + num_docs)):
+ *   [0] item count; items {i, t0, n, doc} at [16 + 4p];
+ *   list lengths at [16 + 4 NI + p]; list of item p at
+ *   [16 + 4 NI + round_up(NI, 4) + 2 * 128 * p + 2e] = {block, mask}, e < length.
+ * q2k as above.
  * --------------------------------------------------------------------------------- */
 int msa_plan(const msa_layout *layout, const int32_t *q2k, void *plan, size_t plan_bytes,
              void *stream);
 
 /* ---------------------------------------------------------------------------------
  * Forward (pull-request page, Design: Q[T,64,128], K/V, q2k -> O[T,64,128] + LSE).
- *   Q: bf16 [T, 64, 128].  Kw, Vw: bf16 [W, 4, 128] from msa_align_kv.  q2k as above.
+ *   Q: bf16 [T, 64, 128].  Kw and Vt from msa_align_kv.  plan from msa_plan.  q2k as
+ *   above.
  *   O: bf16 [T, 64, 128].  LSE: fp32 [T, 64], natural log of the sum of exp(scores),
  *   scores including `scale`; -inf (and O = 0) for a row with no keys.
  * --------------------------------------------------------------------------------- */
-int msa_forward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, const int32_t *q2k,
+int msa_forward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vt, const int32_t *q2k,
                 const msa_layout *layout, const void *plan, float scale, msa_bf16 *O,
                 float *LSE, void *stream);
 
@@ -189,22 +202,24 @@ int msa_build_tasks(const msa_layout *layout, const int32_t *row_ptr, const int3
 
 /* ---------------------------------------------------------------------------------
  * Backward (msa_backward_sm100 API page, run_backward and module summary):
- *   Q, dO: bf16 [T, 64, 128]; Kw, Vw: bf16 [W, 4, 128]; LSE: fp32 [T, 64] from
- *   msa_forward; delta from msa_backward_preprocess; tasks from msa_build_tasks and
- *   `grid` the value it was built with (the launch uses that many workgroups).  Writes dQ bf16 [T, 64, 128] and dK, dV bf16 [T, 4, 128] in
- *   compact token order.  scratch >= msa_bwd_scratch_bytes(layout, dq_accum_mode):
- *   the dQ pool (fp32 or bf16) and fp32 dK/dV pools, zeroed by this call.
+ *   Q, dO: bf16 [T, 64, 128]; Kw, Vw, Kt from msa_align_kv; LSE fp32 [T, 64] from
+ *   msa_forward; delta from msa_backward_preprocess; q2k and plan as given to the
+ *   forward; tasks from msa_build_tasks and `grid` the value it was built with (the
+ *   KV-parallel launch uses that many workgroups).  Writes dQ bf16 [T, 64, 128] and
+ *   dK, dV bf16 [T, 4, 128] in compact token order.  scratch >=
+ *   msa_bwd_scratch_bytes(layout, dq_accum_mode): the dQ pool of the pooled modes and
+ *   fp32 dK/dV pools, zeroed by this call.
  * --------------------------------------------------------------------------------- */
-int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, const msa_bf16 *dO,
-                 const float *LSE, const float *delta, const void *tasks, int32_t grid,
-                 const msa_layout *layout, float scale, int dq_accum_mode, msa_bf16 *dQ,
-                 msa_bf16 *dK, msa_bf16 *dV, void *scratch, size_t scratch_bytes,
-                 void *stream);
+int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, const msa_bf16 *Kt,
+                 const msa_bf16 *dO, const float *LSE, const float *delta, const int32_t *q2k,
+                 const void *plan, const void *tasks, int32_t grid, const msa_layout *layout,
+                 float scale, int dq_accum_mode, msa_bf16 *dQ, msa_bf16 *dK, msa_bf16 *dV,
+                 void *scratch, size_t scratch_bytes, void *stream);
 
 /* Timing hook: if both are non-NULL hipEvent_t handles, every later msa_backward call
- * from this host thread records `start` right before its main KV-parallel kernel and
- * `stop` right after it, on the call's stream (NULL, NULL turns it off).  Lets a caller
- * time that kernel alone with hipEventElapsedTime. */
+ * from this host thread records `start` right before its KV-parallel kernel (dK/dV,
+ * plus dQ atomics in the pooled modes) and `stop` right after it, on the call's
+ * stream; NULL, NULL turns it off.  Lets a caller time that kernel alone. */
 void msa_set_backward_timing_events(void *start, void *stop);
 
 /* Short description of a return code. */

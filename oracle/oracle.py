@@ -175,7 +175,10 @@ def forward_plan(q2k, cu_seqlens, nq: int, blk: int = 128):
     consecutive queries (last one shorter); every index head i has the same groups.
     Each head's groups are ordered by cost = number of member slots, descending, ties
     by document order; the heads are interleaved (item p belongs to head p % HI and is
-    that head's (p // HI)-th item).  Returns int32 [HI*G, 4] and the costs [HI*G]."""
+    that head's (p // HI)-th item).  Each item also carries its walk list: the member
+    blocks of its queries in ascending order, each with the bit mask of the queries
+    (bit u = query t0 + u) that list it.  Returns (items int32 [HI*G, 4], costs
+    [HI*G], lists: list of int32 [len, 2] arrays (block, mask))."""
     q = _i32(q2k)
     HI = q.shape[0]
     cu = _i32(cu_seqlens)
@@ -188,6 +191,7 @@ def forward_plan(q2k, cu_seqlens, nq: int, blk: int = 128):
     G = len(groups)
     items = np.zeros((HI * G, 4), dtype=np.int32)
     costs = np.zeros(HI * G, dtype=np.int32)
+    lists = [None] * (HI * G)
     for i in range(HI):
         c = np.array([per_tok[i, t0:t0 + n].sum() for (t0, n, _) in groups], dtype=np.int64)
         order = sorted(range(G), key=lambda g: (-c[g], g))
@@ -196,7 +200,13 @@ def forward_plan(q2k, cu_seqlens, nq: int, blk: int = 128):
             t0, n, d = groups[g]
             items[p] = (i, t0, n, d)
             costs[p] = c[g]
-    return items, costs
+            masks = {}
+            for u in range(n):
+                for j in np.nonzero(mem[i, t0 + u])[0]:
+                    b = int(q[i, t0 + u, j])
+                    masks[b] = masks.get(b, 0) | (1 << u)
+            lists[p] = np.array(sorted(masks.items()), dtype=np.int32).reshape(-1, 2)
+    return items, costs, lists
 
 
 # --------------------------------------------------------------------------------------

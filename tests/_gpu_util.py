@@ -56,7 +56,7 @@ def check_lse(gpu, ref, mask=None):
     return check_close("LSE", g[~ninf], r[~ninf])
 
 
-def run_gpu(cu, q2k, tens, mode=0, grid=None, backward=True):
+def run_gpu(cu, q2k, tens, mode=2, grid=None, backward=True):
     """Forward (+ backward) of the HIP path on cuda:0.  Returns (msa object, outputs)."""
     M = msa_module()
     dev = "cuda:0"
@@ -83,9 +83,12 @@ def check_structures(m, cu, q2k):
     np.testing.assert_array_equal(rp, orp)
     for r in range(len(orp) - 1):
         np.testing.assert_array_equal(np.sort(cols[rp[r]:rp[r + 1]]), ocols[orp[r]:orp[r + 1]])
-    items = m.plan_items()
-    oitems, _ = OR.forward_plan(q2k, cu, 16)
+    items, lists = m.plan_items()
+    oitems, _, olists = OR.forward_plan(q2k, cu, m.fwd_group)
     np.testing.assert_array_equal(items, oitems)
+    assert len(lists) == len(olists)
+    for a, b in zip(lists, olists):
+        np.testing.assert_array_equal(a, b)
     tk = m.task_tables()
     # the oracle's task builder on the GPU's own CSR order must reproduce the tables
     otk = OR.tasks(rp, cols, cu, 4, m.grid)

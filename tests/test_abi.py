@@ -66,7 +66,9 @@ def test_size_queries(M):
     assert M.msa_tasks_bytes(L, 0) == 0
     f32 = M.msa_bwd_scratch_bytes(L, 0)
     b16 = M.msa_bwd_scratch_bytes(L, 1)
+    rec = M.msa_bwd_scratch_bytes(L, 2)
     assert f32 - b16 == 16384 * 64 * 128 * 2
+    assert rec == 2 * 16384 * 4 * 128 * 4
     assert M.msa_bwd_scratch_bytes(L, 7) == 0
     bad = FakeLayout(M, T=1000, W=1000)  # W not a multiple of 128
     assert M.msa_plan_bytes(bad) == 0
@@ -80,21 +82,21 @@ def test_argument_errors_return_before_device_use(M):
     mis = ctypes.c_void_p(a.value + 4)
     null = None
     E = dict(NULL=1, ALIGN=2, SHAPE=3, SCRATCH=4, MODE=5, GRID=6)
-    assert lib.msa_align_kv(a, a, L.ref(), a, null, None) == E["NULL"]
-    assert lib.msa_align_kv(a, a, L.ref(), a, mis, None) == E["ALIGN"]
+    assert lib.msa_align_kv(a, a, L.ref(), a, null, a, a, None) == E["NULL"]
+    assert lib.msa_align_kv(a, a, L.ref(), a, mis, a, a, None) == E["ALIGN"]
     assert lib.msa_build_k2q_csr(a, L.ref(), a, a, a, a, 1, None) == E["SCRATCH"]
     assert lib.msa_plan(L.ref(), a, a, 16, None) == E["SCRATCH"]
     assert lib.msa_forward(a, a, a, a, L.ref(), a, ctypes.c_float(-1.0), a, a, None) == E["SHAPE"]
     assert lib.msa_backward_preprocess(a, a, 0, a, None) == E["SHAPE"]
     assert lib.msa_build_tasks(L.ref(), a, a, 0, a, 1 << 30, None) == E["GRID"]
-    assert lib.msa_backward(a, a, a, a, a, a, a, 256, L.ref(), ctypes.c_float(0.1), 9, a, a, a, a,
-                            1 << 40, None) == E["MODE"]
-    assert lib.msa_backward(a, a, a, a, a, a, a, 0, L.ref(), ctypes.c_float(0.1), 0, a, a, a, a,
-                            1 << 40, None) == E["GRID"]
-    assert lib.msa_backward(a, a, a, a, a, a, a, 256, L.ref(), ctypes.c_float(0.1), 0, a, a, a, a,
-                            16, None) == E["SCRATCH"]
+    bw = lambda grid, mode, nbytes: lib.msa_backward(a, a, a, a, a, a, a, a, a, a, grid, L.ref(),
+                                                     ctypes.c_float(0.1), mode, a, a, a, a, nbytes, None)
+    assert bw(256, 9, 1 << 40) == E["MODE"]
+    assert bw(0, 2, 1 << 40) == E["GRID"]
+    assert bw(256, 0, 16) == E["SCRATCH"]
+    assert bw(256, 2, 16) == E["SCRATCH"]
     bad = FakeLayout(M, T=1000, W=1000)
-    assert lib.msa_align_kv(a, a, bad.ref(), a, a, None) == E["SHAPE"]
+    assert lib.msa_align_kv(a, a, bad.ref(), a, a, a, a, None) == E["SHAPE"]
     assert lib.msa_status_string(4) == b"buffer smaller than its size query"
 
 

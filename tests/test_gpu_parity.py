@@ -52,11 +52,11 @@ def test_forward_parity_small(name):
     check_lse(to_np(out["LSE"]), LSE)
 
 
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode", [2, 0, 1])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_backward_parity_small(name, mode):
     say("case", name, "dq mode", mode)
-    cu, q2k, tens = _small(name, scatter=(mode == 1))
+    cu, q2k, tens = _small(name, scatter=(mode != 0))
     m, out = run_gpu(cu, q2k, tens, mode=mode)
     Q, K, V, dO = inputs64(tens)
     dQ, dK, dV, _, _ = OR.backward(Q, K, V, dO, q2k, cu, SCALE)
@@ -115,3 +115,18 @@ def test_two_calls_reuse_buffers_and_stay_consistent():
     assert torch.equal(O, out1["O"]) and torch.equal(LSE, out1["LSE"])
     for a, b, n in ((dQ, out1["dQ"], "dQ"), (dK, out1["dK"], "dK"), (dV, out1["dV"], "dV")):
         check_close(n, to_np(a), to_np(b), rel_l2=1e-2, max_abs_frac=1e-2)
+
+
+@pytest.mark.parametrize("name", ["uniform_3docs_ragged", "zipf_many_short"])
+def test_workspace_alignment_bit_exact(name):
+    """Kw/Vw hold each document's rows at its 128-aligned workspace offset, zeros in
+    the padding; Kt/Vt hold the same blocks transposed (keys contiguous)."""
+    cu, q2k, tens = _small(name)
+    m, _ = run_gpu(cu, q2k, tens, backward=False)
+    for X, Xw, Xt in (("K", m.Kw, m.Kt), ("V", m.Vw, m.Vt)):
+        ref = OR.align_kv(tens[X].view(torch.int16).numpy(), cu)
+        got = Xw.view(torch.int16).cpu().numpy()
+        np.testing.assert_array_equal(got, ref)
+        NB = ref.shape[0] // 128
+        blocks = ref.reshape(NB, 128, 4, 128).transpose(2, 0, 3, 1)  # [kv][gb][dim][key]
+        np.testing.assert_array_equal(Xt.view(torch.int16).cpu().numpy().reshape(4, NB, 128, 128), blocks)

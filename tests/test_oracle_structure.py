@@ -119,19 +119,29 @@ def test_tasks_match_brute_force_and_cover_rows(grid):
     assert np.all(cover == 1)
 
 
-def test_forward_plan_partitions_queries_and_orders_by_cost():
+@pytest.mark.parametrize("nq", [8, 16])
+def test_forward_plan_partitions_queries_and_orders_by_cost(nq):
     cu, q2k = WL.make_custom([300, 41, 77, 129], "uniform", 9, num_index_heads=4, topk=7, blk=16)
-    nq = 32
-    items, costs = OR.forward_plan(q2k, cu, nq, blk=16)
+    q2k = WL.scatter_unused(q2k, 3)
+    q2k[1, 20, 0] = q2k[1, 20, 1]  # a repeated id adds nothing
+    items, costs, lists = OR.forward_plan(q2k, cu, nq, blk=16)
     T = int(cu[-1])
     seen = np.zeros((4, T), dtype=int)
     mem = OR.member_slots(q2k, cu, 16).sum(axis=2)
+    _, pos, blk = OR.coords(cu, 16)
     for p, (i, t0, n, d) in enumerate(items):
         assert i == p % 4
         assert cu[d] <= t0 and t0 + n <= cu[d + 1] and 1 <= n <= nq
         assert (t0 - cu[d]) % nq == 0
         seen[i, t0:t0 + n] += 1
         assert costs[p] == mem[i, t0:t0 + n].sum()
+        # walk list: brute force over the items' queries
+        brute = {}
+        for u in range(n):
+            for b in set(int(x) for x in q2k[i, t0 + u] if 0 <= x <= blk[t0 + u]):
+                brute[b] = brute.get(b, 0) | (1 << u)
+        assert [tuple(x) for x in lists[p]] == sorted(brute.items())
+        assert int(sum(bin(m).count("1") for _, m in lists[p])) == costs[p]
     assert np.all(seen == 1)
     for i in range(4):
         c = costs[i::4]
