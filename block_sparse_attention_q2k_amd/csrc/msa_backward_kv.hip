@@ -27,15 +27,8 @@ constexpr int kKvThreads = 256;
 constexpr int kKvTile = 65536;               // Q tile 32 KB + dO tile 32 KB
 constexpr int kKvScalBytes = 3 * 128 * 4;    // lse2[128], delta[128], qpos[128]
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
-
-// v_mfma_f32_32x32x16_bf16: lane l holds A[l%32][8(l/32)+0..7], B[8(l/32)+0..7][l%32];
-// C register r of lane l is C[8(r/4) + 4(l/32) + r%4][l%32].
-__device__ inline f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 // Swizzle of the Q / dO tiles ([128 rows][256 B]): 16-byte chunk c of row r is stored at
 // chunk c ^ f(r), f(r) = ((r & 3) << 2) | ((r >> 2) & 3).  f is a bijection on r % 16,

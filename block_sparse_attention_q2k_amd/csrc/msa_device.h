@@ -56,6 +56,14 @@ __device__ inline f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c)
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// v_mfma_f32_32x32x16_bf16: lane l holds A[l%32][8(l/32)+0..7], B[8(l/32)+0..7][l%32];
+// C register r of lane l is C[8(r/4) + 4(l/32) + r%4][l%32].
+__device__ inline f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // LDS access helpers.  `lds` is the byte offset inside the kernel's LDS block.
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) char lds_char;

@@ -211,67 +211,87 @@ __global__ void row_len_kernel(const int32_t *__restrict__ row_ptr, int n, int32
 // PlanView::lists + 2 * kPlanMaxList * p; aux: gstart [ndocs+1], group info {t0,n,d,_}
 // x Gmax, cost [4 x Gmax].
 
-// Walk list of one item (one wave per item): its queries' member blocks in ascending
-// order with the mask of queries selecting each.  The <= 128 (block, query) keys are
-// bitonic-sorted in LDS; the first key of each block run emits (block, OR of run).
-__global__ void __launch_bounds__(64)
+// Walk list of one item (one workgroup of 256 threads per item): its queries' member
+// blocks in ascending order with the mask of queries selecting each.  The <= 512
+// (block, query) keys are bitonic-sorted in LDS; the first key of each block run emits
+// (block, OR of the run's query bits).
+constexpr int kListThreads = 256;
+__global__ void __launch_bounds__(kListThreads)
 plan_lists_kernel(const int32_t *__restrict__ q2k, const int32_t *__restrict__ cu, int T,
                   const int32_t *__restrict__ plan, int32_t *__restrict__ len,
                   int32_t *__restrict__ lists) {
-  __shared__ int32_t keys[kPlanMaxList];
-  const int p = blockIdx.x, lane = threadIdx.x;
+  constexpr int kSortN = 512;                     // power of two >= kPlanMaxList
+  constexpr int kPer = kSortN / kListThreads;     // keys per thread (2)
+  static_assert(kSortN == 2 * kListThreads && kPlanMaxList <= kSortN && kFwdGroup <= 32,
+                "one compare pair per thread; unit ids fit 5 bits");
+  __shared__ int32_t keys[kSortN];
+  __shared__ int32_t wsum[kListThreads / 64 + 1];
+  const int p = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (p >= plan[0]) return;
   const i32x4 it = ((const i32x4 *)(plan + kPlanHeaderWords))[p];
   const int i = it[0], t0 = it[1], n = it[2], d = it[3];
   const int p0 = t0 - cu[d];
   constexpr int kNone = 0x7fffffff;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int e = lane + 64 * h, u = e >> 4, j = e & 15;
+  for (int h = 0; h < kPer; ++h) {
+    const int e = tid + kListThreads * h, u = e >> 4, j = e & 15;
     int key = kNone;
-    if (u < n) {
+    if (u < n) {  // n <= kFwdGroup, so e < kPlanMaxList
       const int b = q2k[((size_t)i * T + t0 + u) * kTopk + j];
-      if (b >= 0 && b <= (p0 + u) / kBlk) key = (b << 4) | u;
+      if (b >= 0 && b <= (p0 + u) / kBlk) key = (b << 5) | u;
     }
     keys[e] = key;
   }
   __syncthreads();
-  for (int k = 2; k <= kPlanMaxList; k <<= 1)
+  for (int k = 2; k <= kSortN; k <<= 1)
     for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      const int a = (lane / jj) * 2 * jj + (lane % jj), b = a + jj;  // one pair per lane
-      const int ka = keys[a], kb = keys[b];
-      const bool up = (a & k) == 0;
-      if ((ka > kb) == up) {
-        keys[a] = kb;
-        keys[b] = ka;
+      {  // kSortN / 2 compare pairs, one per thread
+        const int q = tid;
+        const int a = (q / jj) * 2 * jj + (q % jj), b = a + jj;
+        const int ka = keys[a], kb = keys[b];
+        const bool up = (a & k) == 0;
+        if ((ka > kb) == up) {
+          keys[a] = kb;
+          keys[b] = ka;
+        }
       }
       __syncthreads();
     }
-  int start[2], mask[2], blk[2];
+  int start[kPer], mask[kPer], blk[kPer];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int e = lane + 64 * h, k = keys[e];
-    blk[h] = k >> 4;
-    start[h] = k != kNone && (e == 0 || (keys[e - 1] >> 4) != blk[h]);
+  for (int h = 0; h < kPer; ++h) {
+    const int e = tid * kPer + h;  // consecutive keys per thread keep the runs in order
+    const int key = keys[e];
+    blk[h] = key >> 5;
+    start[h] = key != kNone && (e == 0 || (keys[e - 1] >> 5) != blk[h]);
     mask[h] = 0;
     if (start[h])
-      for (int f = e; f < kPlanMaxList && keys[f] != kNone && (keys[f] >> 4) == blk[h]; ++f)
-        mask[h] |= 1 << (keys[f] & 15);
+      for (int f = e; f < kSortN && keys[f] != kNone && (keys[f] >> 5) == blk[h]; ++f)
+        mask[h] |= 1 << (keys[f] & 31);
   }
-  const uint64_t b0 = __ballot(start[0]), b1 = __ballot(start[1]);
-  const uint64_t below = (1ull << lane) - 1;
+  int mine = 0;
+#pragma unroll
+  for (int h = 0; h < kPer; ++h) mine += start[h];
+  // exclusive prefix of `mine` over the workgroup (thread order = key order)
+  int incl = mine;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  int r = base + incl - mine;
   int32_t *out = lists + (size_t)2 * kPlanMaxList * p;
-  if (start[0]) {
-    const int r = __popcll(b0 & below);
-    out[2 * r] = blk[0];
-    out[2 * r + 1] = mask[0];
-  }
-  if (start[1]) {
-    const int r = __popcll(b0) + __popcll(b1 & below);
-    out[2 * r] = blk[1];
-    out[2 * r + 1] = mask[1];
-  }
-  if (lane == 0) len[p] = __popcll(b0) + __popcll(b1);
+#pragma unroll
+  for (int h = 0; h < kPer; ++h)
+    if (start[h]) {
+      out[2 * r] = blk[h];
+      out[2 * r + 1] = mask[h];
+      ++r;
+    }
+  if (tid == kListThreads - 1) len[p] = base + incl;
 }
 
 __global__ void __launch_bounds__(1024)
@@ -561,8 +581,8 @@ hipError_t build_plan(const LayoutArgs &L, const int32_t *q2k, void *plan_v, hip
                      q2k, L.cu, L.ndocs, L.T, gmax, v.header, v.gstart, (i32x4 *)v.ginfo, v.cost);
   hipLaunchKernelGGL(plan_sort_kernel, dim3(kHI), dim3(1024), 0, s, gmax, v.header,
                      (const i32x4 *)v.ginfo, v.cost);
-  hipLaunchKernelGGL(plan_lists_kernel, dim3(kHI * gmax), dim3(64), 0, s, q2k, L.cu, L.T, v.header,
-                     v.len, v.lists);
+  hipLaunchKernelGGL(plan_lists_kernel, dim3(kHI * gmax), dim3(kListThreads), 0, s, q2k, L.cu, L.T,
+                     v.header, v.len, v.lists);
   return hipGetLastError();
 }
 

@@ -205,7 +205,9 @@ def forward_plan(q2k, cu_seqlens, nq: int, blk: int = 128):
                 for j in np.nonzero(mem[i, t0 + u])[0]:
                     b = int(q[i, t0 + u, j])
                     masks[b] = masks.get(b, 0) | (1 << u)
-            lists[p] = np.array(sorted(masks.items()), dtype=np.int32).reshape(-1, 2)
+            # masks are 32-bit patterns: bit 31 is stored as the int32 sign bit
+            lists[p] = (np.array(sorted(masks.items()), dtype=np.int64).reshape(-1, 2)
+                        .astype(np.uint32).view(np.int32))
     return items, costs, lists
 
 

@@ -102,6 +102,30 @@ def test_empty_key_set_rows():
     check_lse(L, rL)
 
 
+def test_forward_reference_fallback_rows():
+    """Rows whose later blocks score far above their first block (about 115 nats, so
+    2^(s - m) against the first block's maximum would overflow fp32) take the exact-max
+    second launch of the forward; they and their item neighbours must still match."""
+    say("case fallback_rows_384")
+    cu, q2k = WL.make_custom([384], "all", 5)
+    tens = WL.make_tensors(384, 105)
+    u = torch.full((128,), 1.0 / np.sqrt(128.0))
+    Q = tens["Q"].float()
+    K = tens["K"].float()
+    Q[300:310] = 96.0 * u
+    K[128:132] = 16.0 * u
+    tens = dict(tens, Q=Q.to(torch.bfloat16), K=K.to(torch.bfloat16))
+    m, out = run_gpu(cu, q2k, tens, mode=2)
+    Q64, K64, V64, dO64 = inputs64(tens)
+    O, LSE = OR.forward(Q64, K64, V64, q2k, cu, SCALE)
+    check_close("O", to_np(out["O"]), O)
+    check_lse(to_np(out["LSE"]), LSE)
+    dQ, dK, dV, _, _ = OR.backward(Q64, K64, V64, dO64, q2k, cu, SCALE)
+    check_close("dQ", to_np(out["dQ"]), dQ)
+    check_close("dK", to_np(out["dK"]), dK)
+    check_close("dV", to_np(out["dV"]), dV)
+
+
 def test_two_calls_reuse_buffers_and_stay_consistent():
     """The same MSA object run twice gives the same structures and close gradients
     (atomics make them not bitwise equal)."""

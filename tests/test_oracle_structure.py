@@ -119,7 +119,7 @@ def test_tasks_match_brute_force_and_cover_rows(grid):
     assert np.all(cover == 1)
 
 
-@pytest.mark.parametrize("nq", [8, 16])
+@pytest.mark.parametrize("nq", [8, 16, 28, 32])
 def test_forward_plan_partitions_queries_and_orders_by_cost(nq):
     cu, q2k = WL.make_custom([300, 41, 77, 129], "uniform", 9, num_index_heads=4, topk=7, blk=16)
     q2k = WL.scatter_unused(q2k, 3)
@@ -140,8 +140,9 @@ def test_forward_plan_partitions_queries_and_orders_by_cost(nq):
         for u in range(n):
             for b in set(int(x) for x in q2k[i, t0 + u] if 0 <= x <= blk[t0 + u]):
                 brute[b] = brute.get(b, 0) | (1 << u)
-        assert [tuple(x) for x in lists[p]] == sorted(brute.items())
-        assert int(sum(bin(m).count("1") for _, m in lists[p])) == costs[p]
+        got = [(int(b), int(m) & 0xFFFFFFFF) for b, m in lists[p]]  # masks are 32-bit patterns
+        assert got == sorted(brute.items())
+        assert sum(bin(m).count("1") for _, m in got) == costs[p]
     assert np.all(seen == 1)
     for i in range(4):
         c = costs[i::4]
