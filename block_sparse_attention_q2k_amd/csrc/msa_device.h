@@ -44,8 +44,16 @@ __device__ inline uint16_t f2bf(float x) {
   __bf16 b = (__bf16)x;
   return __builtin_bit_cast(uint16_t, b);
 }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two values in one v_cvt_pk_bf16_f32 (round to nearest even), lo in bits 0..15.
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+// Sum of the two bf16 halves of a plus c (v_dot2c_f32_bf16 against (1, 1)).
+__device__ inline float sum_bf16x2(uint32_t a, float c) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), one, c, false);
 }
 __device__ inline float bf2f(uint16_t u) { return __builtin_bit_cast(float, (uint32_t)u << 16); }
 

@@ -46,7 +46,7 @@ extern "C" {
  * module summary). */
 #define MSA_TILE_QUERIES 8
 /* Forward work item: up to this many consecutive queries of one document. */
-#define MSA_FWD_GROUP 24
+#define MSA_FWD_GROUP 16
 
 typedef uint16_t msa_bf16;
 
@@ -155,7 +155,7 @@ int msa_build_k2q_csr(const int32_t *q2k, const msa_layout *layout, int32_t *row
  * Layout of `plan` (int32 words; NI = 4 * (ceil(T / MSA_FWD_GROUP) + num_docs)):
  *   [0] item count; items {i, t0, n, doc} at [16 + 4p];
  *   list lengths at [16 + 4 NI + p]; list of item p at
- *   [16 + 4 NI + round_up(NI, 4) + 2 * 384 * p + 2e] = {block, mask}, e < length.
+ *   [16 + 4 NI + round_up(NI, 4) + 2 * 256 * p + 2e] = {block, mask}, e < length.
  * q2k as above.
  * --------------------------------------------------------------------------------- */
 int msa_plan(const msa_layout *layout, const int32_t *q2k, void *plan, size_t plan_bytes,
