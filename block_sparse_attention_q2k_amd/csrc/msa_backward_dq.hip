@@ -37,62 +37,59 @@ struct DqCtx {
   char *sS;
 };
 
-// dP tile of the pair (u0, u1), then dS = P (dP - delta) with P = 2^(c s - LSE log2 e)
-// from the S tile st, to the slots s0 + column half.  `two`: the second half holds a
-// unit.
-__device__ __forceinline__ void dq_pair_ds(const DqCtx &x, f32x16 &st, const bf16x8 (&vr)[8], int u0,
-                                           int u1, bool two, int s0, int b) {
-  bf16x8 df[8];
-  load_pair_rows(df, x.sD, u0, u1, x.w);
-  const bool diag = (b == (x.p0 + u0) / kBlk) | (b == (x.p0 + u1) / kBlk);
-  const f32x16 dp = tile32(vr, df);
+// dS = P (dP - delta), P = 2^(c s - LSE log2 e), of a pair's tiles (S in st, dP in dp)
+// to the slots s0 + column half; ld = this lane's column {LSE log2 e, delta}.  On the
+// diagonal block the causal mask zeroes P.  Without a second unit the second half's
+// values land in an unused slot.
+__device__ __forceinline__ void dq_pair_ds(const DqCtx &x, const f32x16 &st, const f32x16 &dp, int u0, int u1,
+                                           bool diag, float2 ld, int s0, int b) {
   const int half = x.w.l32 >> 4;
-  const int u = half ? u1 : u0;
-  const bool valid = !half || two;
-  const int qpos = x.p0 + u;
-  if (diag) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = b * kBlk + 32 * x.w.wave + 8 * (r >> 2) + 4 * x.w.hi + (r & 3);
-      if (key > qpos) st[r] = -INFINITY;
-    }
-  }
-  const float2 ld = *(const float2 *)(x.sLD + 2 * (u * 16 + x.w.l16));
+  const int qpos = x.p0 + (half ? u1 : u0);
   char *srow = x.sS + (s0 + half) * kSlotStride + slot_store_offset(x.w);
+  uint32_t pk[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float ds[4];
+  for (int j = 0; j < 8; ++j) {
+    float ds[2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(st[4 * j + r], x.c, -ld.x));
-      ds[r] = pr * (dp[4 * j + r] - ld.y);
+    for (int e = 0; e < 2; ++e) {
+      const int r = 2 * j + e;
+      float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], x.c, -ld.x));
+      if (diag && b * kBlk + 32 * x.w.wave + 8 * (r >> 2) + 4 * x.w.hi + (r & 3) > qpos) pr = 0.f;
+      ds[e] = pr * (dp[r] - ld.y);
     }
-    if (valid) *(u32x2 *)(srow + 16 * j) = u32x2{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};
+    pk[j] = pack_bf16x2(ds[0], ds[1]);
   }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) *(u32x2 *)(srow + 16 * j) = u32x2{pk[2 * j], pk[2 * j + 1]};
+}
+
+// {LSE log2 e, delta} of this lane's column of the pair (u0, u1).
+__device__ __forceinline__ float2 dq_pair_ld(const DqCtx &x, int u0, int u1) {
+  return *(const float2 *)(x.sLD + 2 * (((x.w.l32 < 16) ? u0 : u1) * 16 + x.w.l16));
+}
+
+__device__ __forceinline__ bool dq_pair_diag(const DqCtx &x, int u0, int u1, int b) {
+  return (b == (x.p0 + u0) / kBlk) | (b == (x.p0 + u1) / kBlk);
 }
 
 // dQ phase of one round: dQ^T[dims 32w.., heads] += K^T dS^T for the nr units of mr,
-// whose dS slots are 0 .. nr - 1 in unit order; the next slot is read while the
-// current unit's MFMAs run.
+// whose dS slots are their ranks in mr.  After a unit's MFMAs are issued, the same
+// registers are refilled with the next slot's fragments.
 __device__ __forceinline__ void dq_accumulate(const DqCtx &x, const bf16x8 (&kt)[2][4], uint32_t mr, int nr,
                                               f32x4 (&acc)[kFwdGroup][2]) {
-  bf16x8 sc[4];
-  load_slot(sc, x.sS, 0, x.w);
+  bf16x8 sf[4];
+  load_slot(sf, x.sS, 0, x.w);
   int k = 0;
 #pragma unroll
   for (int u = 0; u < kFwdGroup; ++u) {
-    if (mr & 1u) {
-      bf16x8 sn[4];
-      load_slot(sn, x.sS, min(k + 1, nr - 1), x.w);
+    if ((mr >> u) & 1u) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int md = 0; md < 2; ++md) acc[u][md] = mfma16(kt[md][kk], sc[kk], acc[u][md]);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) sc[kk] = sn[kk];
+        for (int md = 0; md < 2; ++md) acc[u][md] = mfma16(kt[md][kk], sf[kk], acc[u][md]);
       k = uniform(k + 1);
+      load_slot(sf, x.sS, min(k, nr - 1), x.w);
     }
-    mr = uniform(mr >> 1);
   }
 }
 
@@ -130,24 +127,47 @@ __device__ __forceinline__ void dq_step(const DqCtx &x, int a, const bf16x8 (&kc
     const int u4 = h4 ? pop_unit(ms) : u0;
     const bool h5 = ms != 0;
     const int u5 = h5 ? pop_unit(ms) : u4;
-    // ---- S tiles of the round's pairs (K rows), then dP tiles (V rows) and dS
+    (void)h1; (void)h3; (void)h5;
+    const bool d0 = dq_pair_diag(x, u0, u1, b), d1 = dq_pair_diag(x, u2, u3, b), d2 = dq_pair_diag(x, u4, u5, b);
+    // ---- S tiles of the round's pairs (K rows, Q from LDS); each pair's operand
+    // registers are refilled with the next pair's as soon as its MFMAs are issued
     f32x16 s0t, s1t, s2t;
-    {
-      bf16x8 qf[8];
-      load_pair_rows(qf, x.sQ, u0, u1, x.w);
-      s0t = tile32(kc, qf);
-      if (h2) {
-        load_pair_rows(qf, x.sQ, u2, u3, x.w);
-        s1t = tile32(kc, qf);
-      }
-      if (h4) {
-        load_pair_rows(qf, x.sQ, u4, u5, x.w);
-        s2t = tile32(kc, qf);
-      }
+    bf16x8 f[8];
+    load_pair_rows(f, x.sQ, u0, u1, x.w);
+    s0t = tile32(kc, f);
+    if (h2) {
+      load_pair_rows(f, x.sQ, u2, u3, x.w);
+      s1t = tile32(kc, f);
     }
-    dq_pair_ds(x, s0t, vr, u0, u1, h1, 0, b);
-    if (h2) dq_pair_ds(x, s1t, vr, u2, u3, h3, 2, b);
-    if (h4) dq_pair_ds(x, s2t, vr, u4, u5, h5, 4, b);
+    if (h4) {
+      load_pair_rows(f, x.sQ, u4, u5, x.w);
+      s2t = tile32(kc, f);
+    }
+    // ---- dP tiles (V rows, dO from LDS) and dS
+    load_pair_rows(f, x.sD, u0, u1, x.w);
+    float2 ld = dq_pair_ld(x, u0, u1);
+    {
+      const f32x16 dp = tile32(vr, f);
+      const float2 ldc = ld;
+      if (h2) {
+        load_pair_rows(f, x.sD, u2, u3, x.w);
+        ld = dq_pair_ld(x, u2, u3);
+      }
+      dq_pair_ds(x, s0t, dp, u0, u1, d0, ldc, 0, b);
+    }
+    if (h2) {
+      const f32x16 dp = tile32(vr, f);
+      const float2 ldc = ld;
+      if (h4) {
+        load_pair_rows(f, x.sD, u4, u5, x.w);
+        ld = dq_pair_ld(x, u4, u5);
+      }
+      dq_pair_ds(x, s1t, dp, u2, u3, d1, ldc, 2, b);
+    }
+    if (h4) {
+      const f32x16 dp = tile32(vr, f);
+      dq_pair_ds(x, s2t, dp, u4, u5, d2, ld, 4, b);
+    }
     lds_barrier();
     // ---- dQ phase
     dq_accumulate(x, kt, mround, nr, acc);
