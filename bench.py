@@ -75,6 +75,45 @@ def cpu_baseline(cfg, budget_tokens):
                       "sub-workload), fp64 forward %.1f s + backward %.1f s" % (Tp, cfg, t1 - t0, t2 - t1)}
 
 
+# HBM bytes per launch of the main backward kernels at the headline workload (config 2,
+# dQ recompute), from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by the same counters'
+# reading for a plain copy of known size; valid only for the kernel sources they were
+# taken on (sha256 over the files below).
+TRAFFIC_SOURCES = ["msa_backward_kv.hip", "msa_backward_dq.hip", "msa_walk.h", "msa_device.h", "msa_launch.h"]
+TRAFFIC_RECORD = {"config": 2, "dq_mode": "recompute",
+                  "sha256": "020bd2d01d0c45f4a83b4d716b82796dfa6cdef49c05a512deac4fc296cc340b",
+                  "bytes": 11723887120}  # read 11.255 GB + written 0.469 GB
+
+
+def sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_attention_q2k_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(cfg, dq_mode):
+    r = TRAFFIC_RECORD
+    if r is None or cfg != r["config"] or dq_mode != r["dq_mode"] or sources_digest() != r["sha256"]:
+        return None
+    return r["bytes"]
+
+
+def copy_probe(mib):
+    """A plain device copy of mib MiB, five times: what the HBM byte counters read for
+    it calibrates them (read mib MiB, write mib MiB per launch)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,8 +122,10 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--dq-mode", choices=["recompute", "fp32", "bf16x2"], default="recompute")
     ap.add_argument("--grid", type=int, default=0)
-    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB buffer a few times (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the operator runs on a single MI355X and this "
@@ -92,6 +133,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     import block_sparse_attention_q2k_amd as M
     import workloads as WL
     if not os.path.exists(M._LIB_PATH):
@@ -132,27 +176,48 @@ def main():
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for pair in kev:  # torch creates the HIP event on its first record
-        for e in pair:
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(M.TIMING_EVENTS)] for _ in range(args.steps)]
+    for row in kev:  # torch creates the HIP event on its first record
+        for e in row:
             e.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        M.msa_set_backward_timing_events(kev[k][0], kev[k][1])
+        M.msa_set_timing_events(kev[k])
         step(evs[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    M.msa_set_backward_timing_events(None, None)
+    M.msa_set_timing_events(None)
     fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
     bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    main_ms = [e[0].elapsed_time(e[1]) for e in kev]
+    recompute = mode == M.DQ_RECOMPUTE
+    kern_ms = {"fwd": float(np.mean([e[0].elapsed_time(e[1]) for e in kev])),
+               "kv": float(np.mean([e[2].elapsed_time(e[3]) for e in kev])),
+               "dq": float(np.mean([e[4].elapsed_time(e[5]) for e in kev])) if recompute else 0.0}
     ms_step = elapsed * 1e3 / args.steps
     total_flops = fwd_flops + bwd_flops
     value = total_flops / (ms_step * 1e-3) / 1e12
-    main_avg = float(np.mean(main_ms))
-    achieved = bwd_flops / (main_avg * 1e-3) / 1e12
+    # Main backward: the KV-parallel kernel and (recompute mode) the query-parallel dQ
+    # kernel, back to back; together they do the backward's algorithmic contractions.
+    main_ms = kern_ms["kv"] + kern_ms["dq"]
+    achieved = bwd_flops / (main_ms * 1e-3) / 1e12
     status = int(m.status[0].item())
+    unit = 2.0 * 128 * 128 * 16 * slots  # one 128-dim contraction over all member (row, key) pairs
+    kernels = [
+        {"kernel": "fwd_kernel", "avg_ms": round(kern_ms["fwd"], 4), "algorithmic_tflop": round(2 * unit / 1e12, 4),
+         "executed_tflop": round(2 * unit / 1e12, 4),
+         "frac_mfma_peak": round(2 * unit / (kern_ms["fwd"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        {"kernel": "bwd_kv_kernel" if recompute else "bwd_kernel", "avg_ms": round(kern_ms["kv"], 4),
+         "algorithmic_tflop": round((4 if recompute else 5) * unit / 1e12, 4),
+         "executed_tflop": round((4 if recompute else 5) * unit / 1e12, 4),
+         "frac_mfma_peak": round((4 if recompute else 5) * unit / (kern_ms["kv"] * 1e-3) / 1e12
+                                 / MFMA_BF16_PEAK_TFLOPS, 4)},
+    ]
+    if recompute:
+        kernels.append({"kernel": "dq_kernel", "avg_ms": round(kern_ms["dq"], 4),
+                        "algorithmic_tflop": round(unit / 1e12, 4), "executed_tflop": round(3 * unit / 1e12, 4),
+                        "frac_mfma_peak": round(unit / (kern_ms["dq"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)})
+    traffic = recorded_traffic(args.config, args.dq_mode)
 
     out = {
         "metric": "MSA fwd+bwd effective TFLOP/s + ms/layer at 16k packed tokens, 1 MI355X",
@@ -178,10 +243,11 @@ def main():
         "fwd_frac_mfma_peak": round(fwd_flops / (np.median(fwd_ms) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "bwd_frac_mfma_peak": round(bwd_flops / (np.median(bwd_ms) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "q2k_status": status,
-        "roofline": {"kernel": "bwd_kernel (main KV-parallel backward)", "bound": "mfma",
-                     "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+        "roofline": {"kernel": "main backward: " + " + ".join(k["kernel"] for k in kernels[1:]),
+                     "bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "avg_launch_ms": round(main_avg, 4), "traffic": None},
+                     "avg_launch_ms": round(main_ms, 4), "traffic": traffic},
+        "kernels": kernels,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_tokens)

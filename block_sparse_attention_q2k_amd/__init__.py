@@ -41,7 +41,7 @@ EXPORTS = ["msa_layout_host", "msa_csr_scratch_bytes", "msa_csr_cols_capacity", 
            "msa_tasks_bytes", "msa_bwd_scratch_bytes", "msa_default_grid", "msa_align_kv",
            "msa_build_k2q_csr", "msa_plan", "msa_forward", "msa_backward_preprocess",
            "msa_tasks_meta_offset", "msa_build_tasks", "msa_backward", "msa_status_string",
-           "msa_set_backward_timing_events"]
+           "msa_set_timing_events"]
 
 
 def lib():
@@ -75,7 +75,7 @@ def lib():
             "msa_build_tasks": (I, [LP, P, P, I, P, Z, P]),
             "msa_backward": (I, [P, P, P, P, P, P, P, P, P, P, I, LP, F, I, P, P, P, P, Z, P]),
             "msa_status_string": (ctypes.c_char_p, [I]),
-            "msa_set_backward_timing_events": (None, [P, P]),
+            "msa_set_timing_events": (None, [P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -199,11 +199,18 @@ def msa_backward(Q, Kw, Vw, Kt, dO, LSE, delta, q2k, plan, tasks, grid, layout, 
         scratch.numel() * scratch.element_size(), _stream(stream)))
 
 
-def msa_set_backward_timing_events(start, stop):
-    """start/stop: torch.cuda.Event objects (or None, None to turn the hook off)."""
-    lib().msa_set_backward_timing_events(
-        None if start is None else ctypes.c_void_p(start.cuda_event),
-        None if stop is None else ctypes.c_void_p(stop.cuda_event))
+TIMING_EVENTS = 6
+
+
+def msa_set_timing_events(events):
+    """events: TIMING_EVENTS torch.cuda.Event objects (already recorded once, so that
+    the HIP events exist), or None to turn the hook off."""
+    if events is None:
+        lib().msa_set_timing_events(None)
+        return
+    assert len(events) == TIMING_EVENTS
+    arr = (ctypes.c_void_p * TIMING_EVENTS)(*[e.cuda_event for e in events])
+    lib().msa_set_timing_events(arr)
 
 
 def _bytes(n, device):

@@ -58,7 +58,10 @@ int launch_rc(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH; 
 
 size_t round16(size_t b) { return (b + 15) / 16 * 16; }
 
-thread_local hipEvent_t t_bwd_start = nullptr, t_bwd_stop = nullptr;
+thread_local hipEvent_t t_events[MSA_TIMING_EVENTS] = {};
+
+// Records timing event k on s if the hook is set.
+hipError_t mark(int k, hipStream_t s) { return t_events[k] ? hipEventRecord(t_events[k], s) : hipSuccess; }
 
 }  // namespace
 
@@ -176,7 +179,10 @@ int msa_forward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vt, const
   if (rc) return rc;
   if (!(scale > 0.f) || scale != scale) return MSA_ERR_SHAPE;
   if ((rc = check_device())) return rc;
-  return launch_rc(host::forward(Q, Kw, Vt, q2k, L, plan, scale, O, LSE, (hipStream_t)stream));
+  hipError_t e = mark(0, (hipStream_t)stream);
+  if (e == hipSuccess) e = host::forward(Q, Kw, Vt, q2k, L, plan, scale, O, LSE, (hipStream_t)stream);
+  if (e == hipSuccess) e = mark(1, (hipStream_t)stream);
+  return launch_rc(e);
 }
 
 int msa_backward_preprocess(const msa_bf16 *O, const msa_bf16 *dO, int32_t num_tokens,
@@ -225,8 +231,7 @@ int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, cons
   float *dk_pool = (float *)(sc + dq_bytes);
   float *dv_pool = (float *)(sc + dq_bytes + kv_bytes);
   hipError_t e = host::fill_u32(sc, (dq_bytes + 2 * kv_bytes) / 4, 0u, s);
-  const bool timed = t_bwd_start && t_bwd_stop;
-  if (e == hipSuccess && timed) e = hipEventRecord(t_bwd_start, s);
+  if (e == hipSuccess) e = mark(2, s);
   if (e == hipSuccess) {
     if (pool)
       e = host::backward_main(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dq_accum_mode, sc,
@@ -234,17 +239,19 @@ int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, cons
     else
       e = host::backward_kv(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dk_pool, dv_pool, s);
   }
-  if (e == hipSuccess && timed) e = hipEventRecord(t_bwd_stop, s);
-  if (e == hipSuccess && !pool)
-    e = host::backward_dq(Q, dO, Kw, Vw, Kt, LSE, delta, q2k, L, plan, scale, dQ, s);
+  if (e == hipSuccess) e = mark(3, s);
+  if (!pool) {
+    if (e == hipSuccess) e = mark(4, s);
+    if (e == hipSuccess) e = host::backward_dq(Q, dO, Kw, Vw, Kt, LSE, delta, q2k, L, plan, scale, dQ, s);
+    if (e == hipSuccess) e = mark(5, s);
+  }
   if (e == hipSuccess)
     e = host::finalize(pool ? sc : nullptr, dq_accum_mode, dk_pool, dv_pool, L, dQ, dK, dV, s);
   return launch_rc(e);
 }
 
-void msa_set_backward_timing_events(void *start, void *stop) {
-  t_bwd_start = (hipEvent_t)start;
-  t_bwd_stop = (hipEvent_t)stop;
+void msa_set_timing_events(void *const *events) {
+  for (int k = 0; k < MSA_TIMING_EVENTS; ++k) t_events[k] = events ? (hipEvent_t)events[k] : nullptr;
 }
 
 const char *msa_status_string(int status) {

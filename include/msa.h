@@ -216,11 +216,15 @@ int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, cons
                  float scale, int dq_accum_mode, msa_bf16 *dQ, msa_bf16 *dK, msa_bf16 *dV,
                  void *scratch, size_t scratch_bytes, void *stream);
 
-/* Timing hook: if both are non-NULL hipEvent_t handles, every later msa_backward call
- * from this host thread records `start` right before its KV-parallel kernel (dK/dV,
- * plus dQ atomics in the pooled modes) and `stop` right after it, on the call's
- * stream; NULL, NULL turns it off.  Lets a caller time that kernel alone. */
-void msa_set_backward_timing_events(void *start, void *stop);
+/* Timing hook.  `events` holds MSA_TIMING_EVENTS hipEvent_t handles (or is NULL, which
+ * turns the hook off).  While set, calls from this host thread record, on the call's
+ * stream: events[0] / [1] right before / after the forward kernel launches of
+ * msa_forward; events[2] / [3] around the KV-parallel backward kernel of msa_backward
+ * (dK/dV, plus the dQ atomics of the pooled modes); events[4] / [5] around its dQ kernel
+ * (MSA_DQ_RECOMPUTE only).  The array is copied; the caller keeps the events alive while
+ * the hook is set.  Lets a caller time each kernel alone. */
+#define MSA_TIMING_EVENTS 6
+void msa_set_timing_events(void *const *events);
 
 /* Short description of a return code. */
 const char *msa_status_string(int status);
