@@ -203,8 +203,8 @@ dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ dO,
   const int tid = x.w.tid;
 
   const size_t row = ((size_t)t0 * kH + kHPI * x.i) * kD;
-  rows_to_lds<kDqThreads>(sQ, (const char *)(Q + row), (size_t)kH * kD * 2, n * 16, tid);
-  rows_to_lds<kDqThreads>(sD, (const char *)(dO + row), (size_t)kH * kD * 2, n * 16, tid);
+  rows_to_lds<kDqThreads, kFwdGroup * 16, false>(sQ, (const char *)(Q + row), (size_t)kH * kD * 2, n * 16, tid);
+  rows_to_lds<kDqThreads, kFwdGroup * 16, false>(sD, (const char *)(dO + row), (size_t)kH * kD * 2, n * 16, tid);
   for (int k = tid; k < n * 16; k += kDqThreads) {
     const size_t o = (size_t)(t0 + (k >> 4)) * kH + kHPI * x.i + (k & 15);
     sLD[2 * k] = LSE[o] * kLog2e;

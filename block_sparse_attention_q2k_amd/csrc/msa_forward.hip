@@ -61,10 +61,11 @@ __device__ __forceinline__ void fwd_load_v(const FwdCtx &x, bf16x8 (&v)[2][4], i
   for (int md = 0; md < 2; ++md) load_tslice(v[md], x.Vt, gblk, 32 * x.w.wave + 16 * md, x.w.l16, x.w.g);
 }
 
-// Whether block b is the diagonal block of one of the pair's units (uniform); decided
-// before the tile's MFMAs so that no branch sits between them and the tile's reads.
-__device__ __forceinline__ bool fwd_tile_diag(const FwdCtx &x, int u0, int u1, int b) {
-  return (b == (x.p0 + u0) / kBlk) | (b == (x.p0 + u1) / kBlk);
+// Whether the step's block is the diagonal block of one of the pair's units (uniform;
+// dmask = diag_units of the block); decided before the tile's MFMAs so that no branch
+// sits between them and the tile's reads.
+__device__ __forceinline__ bool fwd_tile_diag(uint32_t dmask, int u0, int u1) {
+  return (((dmask >> u0) | (dmask >> u1)) & 1u) != 0;
 }
 
 // Causal mask of the tile on a diagonal block.
@@ -127,7 +128,7 @@ __device__ __forceinline__ void fwd_pair_load(const FwdCtx &x, FwdPair &pr, uint
   pr.u0 = pop_unit(ms);
   pr.two = ms != 0;
   pr.u1 = pr.two ? pop_unit(ms) : pr.u0;
-  load_pair_rows(pr.q, x.sQ, pr.u0, pr.u1, x.w);
+  load_pair_rows_padded(pr.q, x.sQ, pr.u0, pr.u1, x.w);
   pr.mn = x.sM[((x.w.l32 < 16) ? pr.u0 : pr.u1) * 16 + x.w.l16];
 }
 
@@ -135,7 +136,8 @@ __device__ __forceinline__ void fwd_pair_load(const FwdCtx &x, FwdPair &pr, uint
 // pair's MFMAs are issued (they have read their operands), the same registers are
 // refilled with the next pair's Q rows, which then arrive behind the MFMAs and the
 // current pair's softmax.
-__device__ __forceinline__ void fwd_scores(const FwdCtx &x, const bf16x8 (&k)[8], uint32_t mr, int b) {
+__device__ __forceinline__ void fwd_scores(const FwdCtx &x, const bf16x8 (&k)[8], uint32_t mr, int b,
+                                           uint32_t dmask) {
   FwdPair pr;
   uint32_t ms = mr;
   fwd_pair_load(x, pr, ms);
@@ -143,7 +145,7 @@ __device__ __forceinline__ void fwd_scores(const FwdCtx &x, const bf16x8 (&k)[8]
     const int u0 = pr.u0, u1 = pr.u1;
     const bool two = pr.two;
     const float mn = pr.mn;
-    const bool diag = fwd_tile_diag(x, u0, u1, b);
+    const bool diag = fwd_tile_diag(dmask, u0, u1);
     f32x16 st = tile32(k, pr.q);
     const bool more = ms != 0;
     if (more) fwd_pair_load(x, pr, ms);
@@ -189,8 +191,8 @@ __device__ __forceinline__ void fwd_references(const FwdCtx &x, const bf16x8 (&k
       const bool two = units != 0;
       const int u1 = two ? pop_unit(units) : u0;
       bf16x8 q[8];
-      load_pair_rows(q, x.sQ, u0, u1, x.w);
-      const bool diag = fwd_tile_diag(x, u0, u1, b);
+      load_pair_rows_padded(q, x.sQ, u0, u1, x.w);
+      const bool diag = fwd_tile_diag(diag_units(x.p0, b), u0, u1);
       f32x16 st = tile32(k, q);
           fwd_tile_mask(x, st, u0, u1, b, diag);
       const float mx = fwd_tile_max(st) * x.c;
@@ -211,8 +213,8 @@ __device__ __forceinline__ void fwd_fold_max(const FwdCtx &x, const bf16x8 (&k)[
     const bool two = us != 0;
     const int u1 = two ? pop_unit(us) : u0;
     bf16x8 q[8];
-    load_pair_rows(q, x.sQ, u0, u1, x.w);
-    const bool diag = fwd_tile_diag(x, u0, u1, b);
+    load_pair_rows_padded(q, x.sQ, u0, u1, x.w);
+    const bool diag = fwd_tile_diag(diag_units(x.p0, b), u0, u1);
     f32x16 st = tile32(k, q);
       fwd_tile_mask(x, st, u0, u1, b, diag);
     const float mx = fwd_tile_max(st) * x.c;
@@ -235,25 +237,54 @@ __device__ __forceinline__ void fwd_fold_max(const FwdCtx &x, const bf16x8 (&k)[
   }
 }
 
-// One step of the walk over list entry a with the K registers in kc; the next entry's
-// K registers are loaded into kn.  seen: units whose reference is set.  MAXPASS only
-// folds the block maxima into sM.
+// The walk's position: list entries a (block b, unit mask m) and a + 1 (block bn; the
+// last step's bn is its own block, so that the loads and the wait counts do not depend
+// on the position).  The entries are read two steps ahead of their use.
+struct FwdPos {
+  int b, bn, b2;
+  uint32_t m, mn, m2;
+};
+__device__ __forceinline__ void fwd_pos_init(const FwdCtx &x, FwdPos &q) {
+  q.b = uniform(x.list[0]);
+  q.m = (uint32_t)uniform(x.list[1]);
+  const int a1 = min(1, x.nact - 1);
+  q.bn = uniform(x.list[2 * a1]);
+  q.mn = (uint32_t)uniform(x.list[2 * a1 + 1]);
+}
+// Issues the read of entry a + 2 (clamped to the last entry).
+__device__ __forceinline__ void fwd_pos_fetch(const FwdCtx &x, FwdPos &q, int a) {
+  const int a2 = min(a + 2, x.nact - 1);
+  q.b2 = uniform(x.list[2 * a2]);
+  q.m2 = (uint32_t)uniform(x.list[2 * a2 + 1]);
+}
+__device__ __forceinline__ void fwd_pos_advance(FwdPos &q) {
+  q.b = q.bn; q.m = q.mn;
+  q.bn = q.b2; q.mn = q.m2;
+}
+
+// One step of the walk over list entry a (position q) with the K rows and V^T slices of
+// its block in kc / vc; the next entry's are loaded into kn / vn.  seen: units whose
+// reference is set.  MAXPASS only folds the block maxima into sM.
 template <bool MAXPASS>
-__device__ __forceinline__ void fwd_step(const FwdCtx &x, int a, const bf16x8 (&kc)[8], bf16x8 (&kn)[8],
+__device__ __forceinline__ void fwd_step(const FwdCtx &x, int a, FwdPos &q, const bf16x8 (&kc)[8],
+                                         const bf16x8 (&vc)[2][4], bf16x8 (&kn)[8], bf16x8 (&vn)[2][4],
                                          f32x4 (&acc)[kFwdGroup][2], uint32_t &seen) {
-  const int b = uniform(x.list[2 * a]);
-  const uint32_t m = (uint32_t)uniform(x.list[2 * a + 1]);
+  const int b = q.b;
+  const uint32_t m = q.m;
   const int nu = __popc(m);
-  bf16x8 v[2][4];
-  if (!MAXPASS) fwd_load_v(x, v, b);
-  // unconditional, so that the wait counts before the S phase do not depend on it (the
-  // last step reloads its own block)
-  fwd_load_k(x, kn, a + 1 < x.nact ? uniform(x.list[2 * (a + 1)]) : b);
+  fwd_load_k(x, kn, q.bn);
   if (MAXPASS) {
+    fwd_pos_fetch(x, q, a);
+    WAIT_VMCNT(8);  // this step's K rows
     fwd_fold_max(x, kc, m, b);
     lds_barrier();  // sX is rewritten by the next step
+    fwd_pos_advance(q);
     return;
   }
+  fwd_load_v(x, vn, q.bn);
+  fwd_pos_fetch(x, q, a);
+  WAIT_VMCNT(16);  // this step's K rows and V^T slices (loaded one step ahead)
+  const uint32_t dmask = diag_units(x.p0, b);
   const uint32_t fresh = m & ~seen;
   if (fresh) fwd_references(x, kc, fresh, b);
   seen |= m;
@@ -262,24 +293,29 @@ __device__ __forceinline__ void fwd_step(const FwdCtx &x, int a, const bf16x8 (&
     const uint32_t mround = round_bits(m, r0, kFwdSlots);
     if (r0 > 0) lds_barrier();  // P slots are rewritten
     // ---- S phase: the round's units in pairs, this wave's keys
-    fwd_scores(x, kc, mround, b);
+    fwd_scores(x, kc, mround, b, dmask);
     lds_barrier();
     // ---- PV phase
-    fwd_pv(x, v, mround, nr, acc);
+    fwd_pv(x, vc, mround, nr, acc);
   }
   lds_barrier();  // P slots are rewritten by the next step
+  fwd_pos_advance(q);
 }
 
 // The whole walk over the item's list.  seen0 = ~0 keeps the references already in
 // sM (the exact maxima of the max pass).
 template <bool MAXPASS>
 __device__ __forceinline__ void fwd_walk(const FwdCtx &x, f32x4 (&acc)[kFwdGroup][2], uint32_t seen0) {
-  bf16x8 k0[8], k1[8];
+  if (x.nact <= 0) return;
+  bf16x8 k0[8], k1[8], v0[2][4], v1[2][4];
   uint32_t seen = seen0;
-  if (x.nact > 0) fwd_load_k(x, k0, uniform(x.list[0]));
+  FwdPos q;
+  fwd_pos_init(x, q);
+  fwd_load_k(x, k0, q.b);
+  if (!MAXPASS) fwd_load_v(x, v0, q.b);
   for (int a = 0; a < x.nact; a += 2) {
-    fwd_step<MAXPASS>(x, a, k0, k1, acc, seen);
-    if (a + 1 < x.nact) fwd_step<MAXPASS>(x, a + 1, k1, k0, acc, seen);
+    fwd_step<MAXPASS>(x, a, q, k0, v0, k1, v1, acc, seen);
+    if (a + 1 < x.nact) fwd_step<MAXPASS>(x, a + 1, q, k1, v1, k0, v0, acc, seen);
   }
 }
 
@@ -292,7 +328,7 @@ fwd_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
            const int32_t *__restrict__ cu_ws, int NB, const int32_t *__restrict__ plan,
            const int32_t *__restrict__ plan_len, const int32_t *__restrict__ plan_lists,
            float scale_log2e, uint16_t *__restrict__ O, float *__restrict__ LSE) {
-  __shared__ __attribute__((aligned(16))) char sQ[kFwdGroup * 16 * 256];
+  __shared__ __attribute__((aligned(16))) char sQ[kFwdGroup * 16 * kUnitRow];
   __shared__ __attribute__((aligned(16))) char sP[kFwdSlots * kSlotStride];
   __shared__ float sM[kFwdGroup * 16], sLw[kWalkWaves * 2 * kFwdGroup * 16];
   __shared__ int sBad;
@@ -314,7 +350,8 @@ fwd_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
   const int tid = x.w.tid;
 
   // Q rows of the item (16 rows of 256 B per unit) into sQ
-  rows_to_lds<kWalkThreads>(sQ, (const char *)(Q + ((size_t)t0 * kH + kHPI * x.i) * kD), (size_t)kH * kD * 2, n * 16, tid);
+  rows_to_lds<kWalkThreads, kFwdGroup * 16, true>(sQ, (const char *)(Q + ((size_t)t0 * kH + kHPI * x.i) * kD),
+                                                  (size_t)kH * kD * 2, n * 16, tid);
   for (int k = tid; k < kFwdGroup * 16; k += kWalkThreads) sM[k] = -INFINITY;
   if (tid == 0) sBad = 0;
   __syncthreads();

@@ -21,12 +21,18 @@ constexpr int kWalkThreads = 256;  // 4 waves, one per SIMD
 constexpr int kWalkWaves = kWalkThreads / 64;
 
 // Per-unit LDS slots ([16 heads][128 keys] bf16, P or dS) with rows padded to 272 B, so
-// that the 8-byte stores of a 32 x 32 tile (keys 8 j + 4 hi .. of one row) and the
-// 16-byte B-fragment reads (keys 32 kk + 8 g ..) spread over the banks; +32 B per slot
-// so that the two slots of a pair start on different banks.
+// that the 16-byte B-fragment reads (keys 32 kk + 8 g .., 16 rows) spread over all
+// banks.  Slots are 32 B apart beyond their size; the pad must keep every slot 16-byte
+// aligned (the fragment reads are 16-byte reads: an 8-byte pad made half of them
+// unaligned and the walks about 20 % slower), its size beyond that measured neutral.
 constexpr int kSlotRow = 272;
 constexpr int kSlotBytes = 16 * kSlotRow;
 constexpr int kSlotStride = kSlotBytes + 32;
+
+// Unit rows (a unit's 16 head rows of 256 B) in LDS with rows padded to 272 B: the 16
+// lanes reading one 16-byte chunk of 16 rows cover all banks, and a fragment's offset
+// within the row is the immediate offset of its read.
+constexpr int kUnitRow = 272;
 
 // Per-lane coordinates of the walk.
 struct WalkLane {
@@ -72,6 +78,16 @@ __device__ __forceinline__ uint32_t round_bits(uint32_t m, int r0, int slots) {
   return m ^ rest;
 }
 
+// Bit mask of the units u in [0, 16) whose query (document position p0 + u) lies in
+// block b: the units for which b is the diagonal block.
+__device__ __forceinline__ uint32_t diag_units(int p0, int b) {
+  const int lo = max(0, b * kBlk - p0), hi = min(15, b * kBlk + kBlk - 1 - p0);
+  return lo > hi ? 0u : ((2u << hi) - 1u) & ~((1u << lo) - 1u);
+}
+
+// s_waitcnt vmcnt(n) (n < 64) with no wait on the other counters.
+#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
+
 // Workgroup barrier that publishes LDS data only: waits for this wave's LDS operations
 // (lgkmcnt(0)), not for its global loads still in flight, which __syncthreads() would
 // also wait for.  The empty asm statements keep the compiler from moving memory
@@ -83,16 +99,28 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Rows [0, nrows) of 256 B, row r at src + (r / 16) * unit_stride + (r % 16) * 256 bytes
-// (16 head rows per unit), into LDS at dst + 256 r with chunk c stored at c ^ (r % 16);
-// NT threads.
-template <int NT>
-__device__ __forceinline__ void rows_to_lds(char *dst, const char *src, size_t unit_stride, int nrows,
-                                            int tid) {
+// Rows [0, nrows) (nrows <= MAXROWS) of 256 B, row r at src + (r / 16) * unit_stride +
+// (r % 16) * 256 bytes (16 head rows per unit), into LDS by NT threads.  PADDED: row r
+// at dst + 272 r, chunks in order; otherwise row r at dst + 256 r with chunk c stored at
+// c ^ (r % 16).  All of a thread's loads are issued before its first store, so the
+// copy costs one load latency, not one per row.
+template <int NT, int MAXROWS, bool PADDED>
+__device__ __forceinline__ void rows_to_lds(char *dst, const char *src, size_t unit_stride, int nrows, int tid) {
+  constexpr int kIter = (MAXROWS * 16 + NT - 1) / NT;
   const int q = tid & 15;
-  for (int r = tid >> 4; r < nrows; r += NT / 16)
-    *(u32x4 *)(dst + r * 256 + q * 16) =
-        *(const u32x4 *)(src + (size_t)(r >> 4) * unit_stride + (r & 15) * 256 + ((q ^ (r & 15)) << 4));
+  u32x4 v[kIter];
+#pragma unroll
+  for (int k = 0; k < kIter; ++k) {
+    const int r = (tid >> 4) + k * (NT / 16);
+    if (r < nrows)
+      v[k] = *(const u32x4 *)(src + (size_t)(r >> 4) * unit_stride + (r & 15) * 256 +
+                              (PADDED ? q << 4 : (q ^ (r & 15)) << 4));
+  }
+#pragma unroll
+  for (int k = 0; k < kIter; ++k) {
+    const int r = (tid >> 4) + k * (NT / 16);
+    if (r < nrows) *(u32x4 *)(dst + r * (PADDED ? kUnitRow : 256) + q * 16) = v[k];
+  }
 }
 
 // A operand of a 32 x 32 tile: key rows 32w + l32 of a block (workspace X, KV head kv,
@@ -113,14 +141,22 @@ __device__ __forceinline__ void load_tslice(bf16x8 (&f)[4], const uint16_t *__re
   for (int kk = 0; kk < 4; ++kk) f[kk] = *(const bf16x8 *)(row + 32 * kk);
 }
 
-// B operand of a 32 x 32 tile for the pair (u0, u1) from unit rows in LDS (rows_to_lds
-// layout): lane l32 < 16 reads unit u0, the others u1; f[ks] = row[head l16][dims
+// B operand of a 32 x 32 tile for the pair (u0, u1) from unit rows in LDS (rows_to_lds,
+// swizzled layout): lane l32 < 16 reads unit u0, the others u1; f[ks] = row[head l16][dims
 // 16 ks + 8 hi .. + 7].
 __device__ __forceinline__ void load_pair_rows(bf16x8 (&f)[8], const char *s, int u0, int u1,
                                                const WalkLane &w) {
   const char *row = s + (((w.l32 < 16) ? u0 : u1) * 16 + w.l16) * 256;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) f[ks] = *(const bf16x8 *)(row + w.roff[ks]);
+}
+
+// load_pair_rows for unit rows in the padded layout (rows_to_lds with PADDED).
+__device__ __forceinline__ void load_pair_rows_padded(bf16x8 (&f)[8], const char *s, int u0, int u1,
+                                                      const WalkLane &w) {
+  const char *row = s + (((w.l32 < 16) ? u0 : u1) * 16 + w.l16) * kUnitRow + 16 * w.hi;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) f[ks] = *(const bf16x8 *)(row + 32 * ks);
 }
 
 // 32 x 32 tile t = A B over 128 dims: t[r] = tile[key 32w + 8 (r/4) + 4 hi + r%4][column
