@@ -38,7 +38,8 @@
 
 namespace msa {
 
-constexpr int kFwdSlots = 16;  // P slots: active units per round
+constexpr int kFwdSlots = kFwdGroup;  // P slots: one per unit of the item
+static_assert(kFwdGroup <= 32, "unit masks are 32-bit");
 
 struct FwdCtx {
   WalkLane w;
@@ -55,10 +56,26 @@ __device__ __forceinline__ void fwd_load_k(const FwdCtx &x, bf16x8 (&k)[8], int 
   load_key_rows(k, x.Kw, (size_t)x.wsrow0 + (size_t)b * kBlk, x.i, x.w);
 }
 
+// Half H (dims 64 H .. + 63) of the K rows of block b: k[4 H .. 4 H + 3].
+template <int H>
+__device__ __forceinline__ void fwd_load_k_half(const FwdCtx &x, bf16x8 (&k)[8], int b) {
+  const uint16_t *row =
+      x.Kw + (((size_t)x.wsrow0 + (size_t)b * kBlk + 32 * x.w.wave + x.w.l32) * kHKV + x.i) * kD + 8 * x.w.hi;
+#pragma unroll
+  for (int ks = 4 * H; ks < 4 * H + 4; ++ks) k[ks] = *(const bf16x8 *)(row + 16 * ks);
+}
+
 __device__ __forceinline__ void fwd_load_v(const FwdCtx &x, bf16x8 (&v)[2][4], int b) {
   const size_t gblk = (size_t)x.i * x.NB + (size_t)(x.wsrow0 / kBlk + b);
 #pragma unroll
   for (int md = 0; md < 2; ++md) load_tslice(v[md], x.Vt, gblk, 32 * x.w.wave + 16 * md, x.w.l16, x.w.g);
+}
+
+// V^T slice md (dims 32 w + 16 md ..) of block b.
+template <int MD>
+__device__ __forceinline__ void fwd_load_v_half(const FwdCtx &x, bf16x8 (&v)[2][4], int b) {
+  const size_t gblk = (size_t)x.i * x.NB + (size_t)(x.wsrow0 / kBlk + b);
+  load_tslice(v[MD], x.Vt, gblk, 32 * x.w.wave + 16 * MD, x.w.l16, x.w.g);
 }
 
 // Whether the step's block is the diagonal block of one of the pair's units (uniform;
@@ -132,7 +149,7 @@ __device__ __forceinline__ void fwd_pair_load(const FwdCtx &x, FwdPair &pr, uint
   pr.mn = x.sM[((x.w.l32 < 16) ? pr.u0 : pr.u1) * 16 + x.w.l16];
 }
 
-// S phase of one round (units mr): pairs in unit order at slots 0, 2, 4, ...  Once a
+// S phase of one step (units mr): pairs in unit order at slots 0, 2, 4, ...  Once a
 // pair's MFMAs are issued (they have read their operands), the same registers are
 // refilled with the next pair's Q rows, which then arrive behind the MFMAs and the
 // current pair's softmax.
@@ -163,7 +180,7 @@ __device__ __forceinline__ void fwd_pv_mfma(const bf16x8 (&v)[2][4], const bf16x
     for (int md = 0; md < 2; ++md) acc[md] = mfma16(v[md][kk], pf[kk], acc[md]);
 }
 
-// PV phase of one round: O^T[dims 32w.., heads] += V^T P^T for the nr units of mr,
+// PV phase of one step: O^T[dims 32w.., heads] += V^T P^T for the nr units of mr,
 // whose P slots are their ranks in mr.  After a unit's MFMAs are issued, the same
 // registers are refilled with the next slot's fragments.
 __device__ __forceinline__ void fwd_pv(const FwdCtx &x, const bf16x8 (&v)[2][4], uint32_t mr, int nr,
@@ -272,8 +289,8 @@ __device__ __forceinline__ void fwd_step(const FwdCtx &x, int a, FwdPos &q, cons
   const int b = q.b;
   const uint32_t m = q.m;
   const int nu = __popc(m);
-  fwd_load_k(x, kn, q.bn);
   if (MAXPASS) {
+    fwd_load_k(x, kn, q.bn);
     fwd_pos_fetch(x, q, a);
     WAIT_VMCNT(8);  // this step's K rows
     fwd_fold_max(x, kc, m, b);
@@ -281,23 +298,26 @@ __device__ __forceinline__ void fwd_step(const FwdCtx &x, int a, FwdPos &q, cons
     fwd_pos_advance(q);
     return;
   }
-  fwd_load_v(x, vn, q.bn);
+  // The next block's operands are requested in four groups of four loads spread over
+  // the step (K rows before and after the S phase, V^T slices before and after the PV
+  // phase): issued together right after a barrier, the loads of all waves queue up and
+  // stall the waves' instruction streams until they are accepted.
+  fwd_load_k_half<0>(x, kn, q.bn);
   fwd_pos_fetch(x, q, a);
-  WAIT_VMCNT(16);  // this step's K rows and V^T slices (loaded one step ahead)
+  WAIT_VMCNT(12);  // this step's K rows (issued in the previous step)
   const uint32_t dmask = diag_units(x.p0, b);
   const uint32_t fresh = m & ~seen;
   if (fresh) fwd_references(x, kc, fresh, b);
   seen |= m;
-  for (int r0 = 0; r0 < nu; r0 += kFwdSlots) {
-    const int nr = min(kFwdSlots, nu - r0);
-    const uint32_t mround = round_bits(m, r0, kFwdSlots);
-    if (r0 > 0) lds_barrier();  // P slots are rewritten
-    // ---- S phase: the round's units in pairs, this wave's keys
-    fwd_scores(x, kc, mround, b, dmask);
-    lds_barrier();
-    // ---- PV phase
-    fwd_pv(x, vc, mround, nr, acc);
-  }
+  // ---- S phase: the step's units in pairs, this wave's keys (one slot per unit)
+  fwd_scores(x, kc, m, b, dmask);
+  fwd_load_k_half<1>(x, kn, q.bn);
+  lds_barrier();
+  fwd_load_v_half<0>(x, vn, q.bn);
+  WAIT_VMCNT(12);  // this step's V^T slices
+  // ---- PV phase
+  fwd_pv(x, vc, m, nu, acc);
+  fwd_load_v_half<1>(x, vn, q.bn);
   lds_barrier();  // P slots are rewritten by the next step
   fwd_pos_advance(q);
 }
