@@ -93,84 +93,96 @@ __device__ __forceinline__ void dq_accumulate(const DqCtx &x, const bf16x8 (&kt)
   }
 }
 
-// One step over list entry a with the K rows of this step in kc; the next entry's go to
-// kn.
-__device__ __forceinline__ void dq_step(const DqCtx &x, int a, const bf16x8 (&kc)[8], bf16x8 (&kn)[8],
-                                        f32x4 (&acc)[kFwdGroup][2]) {
-  const int b = uniform(x.list[2 * a]);
-  const uint32_t m = (uint32_t)uniform(x.list[2 * a + 1]);
-  const int nu = __popc(m);
-  const size_t row0 = (size_t)x.wsrow0 + (size_t)b * kBlk;
-  // in the order they are needed: V rows (dP), K^T (dQ phase), next K rows
-  bf16x8 vr[8], kt[2][4];
-  load_key_rows(vr, x.Vw, row0, x.i, x.w);
-  {
+// One round of a step over block b (units mround, nr of them, slots = their ranks):
+// dP tiles of the round's pairs (V rows vc, dO from LDS), then S tiles (K rows kr, Q
+// from LDS) and dS to the slots, a barrier, and the dQ phase with the K^T slices kt.
+// Each pair's LDS operand registers are refilled with the next pair's as soon as its
+// MFMAs are issued.  FIRST: the step's first round, which also issues the step's later
+// loads at fixed points (K^T of this block after the dP tiles, the next block's V rows
+// after the S tiles), so that they are not requested in one burst with the K rows.
+template <bool FIRST>
+__device__ __forceinline__ void dq_round(const DqCtx &x, uint32_t mround, int nr, int b, int bn,
+                                         const bf16x8 (&kr)[8], const bf16x8 (&vc)[8], bf16x8 (&kt)[2][4],
+                                         bf16x8 (&vn)[8], f32x4 (&acc)[kFwdGroup][2]) {
+  uint32_t ms = mround;
+  const int u0 = pop_unit(ms);
+  const bool h1 = ms != 0;
+  const int u1 = h1 ? pop_unit(ms) : u0;
+  const bool h2 = ms != 0;
+  const int u2 = h2 ? pop_unit(ms) : u0;
+  const bool h3 = ms != 0;
+  const int u3 = h3 ? pop_unit(ms) : u2;
+  const bool h4 = ms != 0;
+  const int u4 = h4 ? pop_unit(ms) : u0;
+  const bool h5 = ms != 0;
+  const int u5 = h5 ? pop_unit(ms) : u4;
+  (void)h1; (void)h3; (void)h5;
+  const bool d0 = dq_pair_diag(x, u0, u1, b), d1 = dq_pair_diag(x, u2, u3, b), d2 = dq_pair_diag(x, u4, u5, b);
+  // ---- dP tiles (V rows, dO from LDS)
+  f32x16 p0t, p1t, p2t;
+  bf16x8 f[8];
+  load_pair_rows(f, x.sD, u0, u1, x.w);
+  p0t = tile32(vc, f);
+  if (h2) {
+    load_pair_rows(f, x.sD, u2, u3, x.w);
+    p1t = tile32(vc, f);
+  }
+  if (h4) {
+    load_pair_rows(f, x.sD, u4, u5, x.w);
+    p2t = tile32(vc, f);
+  }
+  if (FIRST) {
     const size_t gblk = (size_t)x.i * x.NB + (size_t)(x.wsrow0 / kBlk + b);
 #pragma unroll
     for (int md = 0; md < 2; ++md) load_tslice(kt[md], x.Kt, gblk, 32 * x.w.wave + 16 * md, x.w.l16, x.w.g);
+    WAIT_VMCNT(8);  // this block's K rows (the K^T slices may be in flight)
   }
-  load_key_rows(kn, x.Kw, (size_t)x.wsrow0 + (size_t)(a + 1 < x.nact ? uniform(x.list[2 * (a + 1)]) : b) * kBlk,
-                x.i, x.w);
-  for (int r0 = 0; r0 < nu; r0 += kDqSlots) {
-    const int nr = min(kDqSlots, nu - r0);
-    const uint32_t mround = round_bits(m, r0, kDqSlots);
-    if (r0 > 0) lds_barrier();  // dS slots are rewritten
-    uint32_t ms = mround;
-    const int u0 = pop_unit(ms);
-    const bool h1 = ms != 0;
-    const int u1 = h1 ? pop_unit(ms) : u0;
-    const bool h2 = ms != 0;
-    const int u2 = h2 ? pop_unit(ms) : u0;
-    const bool h3 = ms != 0;
-    const int u3 = h3 ? pop_unit(ms) : u2;
-    const bool h4 = ms != 0;
-    const int u4 = h4 ? pop_unit(ms) : u0;
-    const bool h5 = ms != 0;
-    const int u5 = h5 ? pop_unit(ms) : u4;
-    (void)h1; (void)h3; (void)h5;
-    const bool d0 = dq_pair_diag(x, u0, u1, b), d1 = dq_pair_diag(x, u2, u3, b), d2 = dq_pair_diag(x, u4, u5, b);
-    // ---- S tiles of the round's pairs (K rows, Q from LDS); each pair's operand
-    // registers are refilled with the next pair's as soon as its MFMAs are issued
-    f32x16 s0t, s1t, s2t;
-    bf16x8 f[8];
-    load_pair_rows(f, x.sQ, u0, u1, x.w);
-    s0t = tile32(kc, f);
+  // ---- S tiles (K rows, Q from LDS) and dS
+  load_pair_rows(f, x.sQ, u0, u1, x.w);
+  float2 ld = dq_pair_ld(x, u0, u1);
+  {
+    const f32x16 st = tile32(kr, f);
+    const float2 ldc = ld;
     if (h2) {
       load_pair_rows(f, x.sQ, u2, u3, x.w);
-      s1t = tile32(kc, f);
+      ld = dq_pair_ld(x, u2, u3);
     }
+    dq_pair_ds(x, st, p0t, u0, u1, d0, ldc, 0, b);
+  }
+  if (h2) {
+    const f32x16 st = tile32(kr, f);
+    const float2 ldc = ld;
     if (h4) {
       load_pair_rows(f, x.sQ, u4, u5, x.w);
-      s2t = tile32(kc, f);
+      ld = dq_pair_ld(x, u4, u5);
     }
-    // ---- dP tiles (V rows, dO from LDS) and dS
-    load_pair_rows(f, x.sD, u0, u1, x.w);
-    float2 ld = dq_pair_ld(x, u0, u1);
-    {
-      const f32x16 dp = tile32(vr, f);
-      const float2 ldc = ld;
-      if (h2) {
-        load_pair_rows(f, x.sD, u2, u3, x.w);
-        ld = dq_pair_ld(x, u2, u3);
-      }
-      dq_pair_ds(x, s0t, dp, u0, u1, d0, ldc, 0, b);
-    }
-    if (h2) {
-      const f32x16 dp = tile32(vr, f);
-      const float2 ldc = ld;
-      if (h4) {
-        load_pair_rows(f, x.sD, u4, u5, x.w);
-        ld = dq_pair_ld(x, u4, u5);
-      }
-      dq_pair_ds(x, s1t, dp, u2, u3, d1, ldc, 2, b);
-    }
-    if (h4) {
-      const f32x16 dp = tile32(vr, f);
-      dq_pair_ds(x, s2t, dp, u4, u5, d2, ld, 4, b);
-    }
-    lds_barrier();
-    // ---- dQ phase
-    dq_accumulate(x, kt, mround, nr, acc);
+    dq_pair_ds(x, st, p1t, u2, u3, d1, ldc, 2, b);
+  }
+  if (h4) {
+    const f32x16 st = tile32(kr, f);
+    dq_pair_ds(x, st, p2t, u4, u5, d2, ld, 4, b);
+  }
+  if (FIRST) load_key_rows(vn, x.Vw, (size_t)x.wsrow0 + (size_t)bn * kBlk, x.i, x.w);
+  lds_barrier();
+  if (FIRST) WAIT_VMCNT(8);  // this block's K^T slices (the next V rows may be in flight)
+  // ---- dQ phase
+  dq_accumulate(x, kt, mround, nr, acc);
+}
+
+// One step over list entry a (block b, units m; the next entry's block bn) with this
+// block's V rows in vc (loaded one step ahead); the next block's go to vn.  The K rows
+// of the block are loaded at the start of the step and first needed after the dP
+// tiles.
+__device__ __forceinline__ void dq_step(const DqCtx &x, int b, uint32_t m, int bn, const bf16x8 (&vc)[8],
+                                        bf16x8 (&vn)[8], f32x4 (&acc)[kFwdGroup][2]) {
+  const int nu = __popc(m);
+  bf16x8 kr[8], kt[2][4];
+  load_key_rows(kr, x.Kw, (size_t)x.wsrow0 + (size_t)b * kBlk, x.i, x.w);
+  WAIT_VMCNT(8);  // this block's V rows (the K rows may be in flight)
+  dq_round<true>(x, round_bits(m, 0, kDqSlots), min(kDqSlots, nu), b, bn, kr, vc, kt, vn, acc);
+  for (int r0 = kDqSlots; r0 < nu; r0 += kDqSlots) {
+    lds_barrier();  // dS slots are rewritten
+    dq_round<false>(x, round_bits(m, r0, kDqSlots), min(kDqSlots, nu - r0), b, bn, kr, vc, kt, vn, acc);
   }
   lds_barrier();  // dS slots are rewritten by the next step
 }
@@ -215,11 +227,29 @@ dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ dO,
   f32x4 acc[kFwdGroup][2];
 #pragma unroll
   for (int u = 0; u < kFwdGroup; ++u) acc[u][0] = acc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 k0[8], k1[8];
-  if (x.nact > 0) load_key_rows(k0, Kw, (size_t)x.wsrow0 + (size_t)uniform(x.list[0]) * kBlk, x.i, x.w);
-  for (int a = 0; a < x.nact; a += 2) {
-    dq_step(x, a, k0, k1, acc);
-    if (a + 1 < x.nact) dq_step(x, a + 1, k1, k0, acc);
+  // the walk: list entries are read one step ahead of their use (entries past the
+  // end repeat the last block, so that the loads do not depend on the position)
+  if (x.nact > 0) {
+    bf16x8 v0[8], v1[8];
+    int b = uniform(x.list[0]);
+    uint32_t m = (uint32_t)uniform(x.list[1]);
+    const int e1 = min(1, x.nact - 1);
+    int bn = uniform(x.list[2 * e1]);
+    uint32_t mn = (uint32_t)uniform(x.list[2 * e1 + 1]);
+    load_key_rows(v0, Vw, (size_t)x.wsrow0 + (size_t)b * kBlk, x.i, x.w);
+    for (int a = 0; a < x.nact; a += 2) {
+      int e2 = min(a + 2, x.nact - 1);
+      int b2 = uniform(x.list[2 * e2]);
+      uint32_t m2 = (uint32_t)uniform(x.list[2 * e2 + 1]);
+      dq_step(x, b, m, bn, v0, v1, acc);
+      b = bn; m = mn; bn = b2; mn = m2;
+      if (a + 1 >= x.nact) break;
+      e2 = min(a + 3, x.nact - 1);
+      b2 = uniform(x.list[2 * e2]);
+      m2 = (uint32_t)uniform(x.list[2 * e2 + 1]);
+      dq_step(x, b, m, bn, v1, v0, acc);
+      b = bn; m = mn; bn = b2; mn = m2;
+    }
   }
   // ---- epilogue: acc[u][md][r] = dQ^T[dim 32w + 16md + 4g + r][head l16] / scale
 #pragma unroll
