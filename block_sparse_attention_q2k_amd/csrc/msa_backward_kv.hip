@@ -57,17 +57,20 @@ __device__ __forceinline__ void kv_row_ids(KvRowIds &ids, const int32_t *__restr
   }
 }
 
-// Issue the asynchronous gather of one task row into `tile`: chunk p = 256 k + tid of
-// each 32 KB half is row 16 k + hh (query k, head hh = tid / 16), physical chunk
-// tid % 16, which holds logical chunk (tid % 16) ^ kv_f(hh) (the swizzle of swz_kv()).
-__device__ __forceinline__ void kv_gather(const uint16_t *__restrict__ Q,
-                                          const uint16_t *__restrict__ dO, const KvRowIds &ids,
-                                          int i, char *tile, int tid) {
+// Issue part of the asynchronous gather of one task row into `tile`: queries
+// 4 half + J0 .. + 1 of the row (Q and dO).  Chunk p = 256 k + tid of each 32 KB half
+// of the tile is row 16 k + hh (query k, head hh = tid / 16), physical chunk tid % 16,
+// which holds logical chunk (tid % 16) ^ kv_f(hh) (the swizzle of swz_kv()).
+template <int J0>
+__device__ __forceinline__ void kv_gather_part(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ dO,
+                                               const KvRowIds &ids, int i, char *tile, int tid, int half) {
   const int wave = tid >> 6, hh = tid >> 4, c = (tid & 15) ^ kv_f(hh);
   lds_char *base = (lds_char *)tile + wave * 1024;
 #pragma unroll
-  for (int k = 0; k < kTileQ; ++k) {
-    const size_t src = ((size_t)ids.t[k] * kH + kHPI * i + hh) * kD + c * 8;
+  for (int j = J0; j < J0 + 2; ++j) {
+    const int k = 4 * half + j;
+    const int t = half ? ids.t[4 + j] : ids.t[j];
+    const size_t src = ((size_t)t * kH + kHPI * i + hh) * kD + c * 8;
     __builtin_amdgcn_global_load_lds((const gvoid *)(Q + src), (lvoid *)(base + k * 4096), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((const gvoid *)(dO + src), (lvoid *)(base + 32768 + k * 4096), 16, 0, 0);
   }
@@ -141,18 +144,21 @@ __device__ __forceinline__ void kv_row(
       for (int e = 0; e < 16; ++e) st.dkacc[nd][e] = st.dvacc[nd][e] = 0.f;
     wait_vm();  // rare; keeps later waits from covering the asynchronous gather
   }
-  // 2. prefetch row + 1: scalars into registers, Q/dO tiles into `nxt` (asynchronous)
+  // 2. prefetch row + 1: scalars into registers now, Q/dO tiles into `nxt`
+  //    (asynchronous) in four parts spread over the compute: issued together right
+  //    after the barrier, the gathers of all waves would queue up and stall the waves'
+  //    instruction streams until accepted.
   const bool more = row + 1 < hi;
+  KvRowIds ids;
   if (more) {
-    KvRowIds ids;
     kv_row_ids(ids, qrows, qpos, row + 1, meta[row + 1][1]);
     if (tid < 128) kv_scalars(LSE, Delta, ids, i, tid, st.lse2, st.del, st.pos);
-    kv_gather(Q, dO, ids, i, nxt, tid);
   }
   // 3. compute
   const int kp = st.kbase + 32 * wave + l32;  // document-local position of this lane's key
 #pragma unroll 1
   for (int half = 0; half < 2; ++half) {
+    if (more) kv_gather_part<0>(Q, dO, ids, i, nxt, tid, half);
     f32x16 sacc[2], pacc[2];
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2) {
@@ -166,6 +172,7 @@ __device__ __forceinline__ void kv_row(
         pacc[m2] = mfma32(*(const bf16x8 *)(cur + 32768 + off), st.vf[ks], pacc[m2]);
       }
     }
+    if (more) kv_gather_part<2>(Q, dO, ids, i, nxt, tid, half);
     // P, dS: register e of sacc[m2] is row 32mt + 8(e/4) + 4h + e%4
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2) {
@@ -254,7 +261,11 @@ bwd_kv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
         kv_scalars(LSE, Delta, ids, i, tid, st.lse2, st.del, st.pos);
         kv_store_scalars(sc0, tid, st.lse2, st.del, st.pos);
       }
-      kv_gather(Q, dO, ids, i, tile0, tid);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        kv_gather_part<0>(Q, dO, ids, i, tile0, tid, half);
+        kv_gather_part<2>(Q, dO, ids, i, tile0, tid, half);
+      }
       wait_vm();
       __syncthreads();
     }
