@@ -84,11 +84,12 @@ bwd_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
         // K/V slices of this wave as B operands: lane (key 32w + 16nt + l16, g)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          const size_t krow = ((size_t)(gb * kBlk + 32 * wave + 16 * nt + l16) * kHKV + i) * kD + 8 * g;
+          const size_t fb = ((size_t)i * NB + gb) * kFragBlock;
+          const int key = 32 * wave + 16 * nt + l16;
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
-            kf[nt][kk] = *(const bf16x8 *)(Kw + krow + 32 * kk);
-            vf[nt][kk] = *(const bf16x8 *)(Vw + krow + 32 * kk);
+            kf[nt][kk] = *(const bf16x8 *)(Kw + fb + frag_row_off(key, 32 * kk + 8 * g));
+            vf[nt][kk] = *(const bf16x8 *)(Vw + fb + frag_row_off(key, 32 * kk + 8 * g));
           }
         }
         // whole K block -> LDS (the dQ product reads K^T from it); wait until every wave
@@ -97,7 +98,7 @@ bwd_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int id = tid + kBwdThreads * k, rr = id >> 4, cc = id & 15;
-          const size_t src = ((size_t)(gb * kBlk + rr) * kHKV + i) * kD + cc * 8;
+          const size_t src = ((size_t)i * NB + gb) * kFragBlock + frag_row_off(rr, cc * 8);
           *(u32x4 *)(smem + kBsK + swz(rr, cc * 16)) = *(const u32x4 *)(Kw + src);
         }
       }

@@ -134,7 +134,7 @@ __device__ __forceinline__ void dq_round(const DqCtx &x, uint32_t mround, int nr
   if (FIRST) {
     const size_t gblk = (size_t)x.i * x.NB + (size_t)(x.wsrow0 / kBlk + b);
 #pragma unroll
-    for (int md = 0; md < 2; ++md) load_tslice(kt[md], x.Kt, gblk, 32 * x.w.wave + 16 * md, x.w.l16, x.w.g);
+    for (int md = 0; md < 2; ++md) load_tslice(kt[md], x.Kt, gblk, 32 * x.w.wave + 16 * md, x.w);
     WAIT_VMCNT(8);  // this block's K rows (the K^T slices may be in flight)
   }
   // ---- S tiles (K rows, Q from LDS) and dS
@@ -162,7 +162,7 @@ __device__ __forceinline__ void dq_round(const DqCtx &x, uint32_t mround, int nr
     const f32x16 st = tile32(kr, f);
     dq_pair_ds(x, st, p2t, u4, u5, d2, ld, 4, b);
   }
-  if (FIRST) load_key_rows(vn, x.Vw, (size_t)x.wsrow0 + (size_t)bn * kBlk, x.i, x.w);
+  if (FIRST) load_key_rows(vn, x.Vw, (size_t)x.i * x.NB + (size_t)(x.wsrow0 / kBlk + bn), x.w);
   lds_barrier();
   if (FIRST) WAIT_VMCNT(8);  // this block's K^T slices (the next V rows may be in flight)
   // ---- dQ phase
@@ -177,7 +177,7 @@ __device__ __forceinline__ void dq_step(const DqCtx &x, int b, uint32_t m, int b
                                         bf16x8 (&vn)[8], f32x4 (&acc)[kFwdGroup][2]) {
   const int nu = __popc(m);
   bf16x8 kr[8], kt[2][4];
-  load_key_rows(kr, x.Kw, (size_t)x.wsrow0 + (size_t)b * kBlk, x.i, x.w);
+  load_key_rows(kr, x.Kw, (size_t)x.i * x.NB + (size_t)(x.wsrow0 / kBlk + b), x.w);
   WAIT_VMCNT(8);  // this block's V rows (the K rows may be in flight)
   dq_round<true>(x, round_bits(m, 0, kDqSlots), min(kDqSlots, nu), b, bn, kr, vc, kt, vn, acc);
   for (int r0 = kDqSlots; r0 < nu; r0 += kDqSlots) {
@@ -236,7 +236,7 @@ dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ dO,
     const int e1 = min(1, x.nact - 1);
     int bn = uniform(x.list[2 * e1]);
     uint32_t mn = (uint32_t)uniform(x.list[2 * e1 + 1]);
-    load_key_rows(v0, Vw, (size_t)x.wsrow0 + (size_t)b * kBlk, x.i, x.w);
+    load_key_rows(v0, Vw, (size_t)x.i * x.NB + (size_t)(x.wsrow0 / kBlk + b), x.w);
     for (int a = 0; a < x.nact; a += 2) {
       int e2 = min(a + 2, x.nact - 1);
       int b2 = uniform(x.list[2 * e2]);

@@ -132,11 +132,12 @@ __device__ __forceinline__ void kv_row(
     st.gb = r - i * NB;
     const int dd = upper_index(cu_ws, ndocs - 1, st.gb * kBlk);
     st.kbase = st.gb * kBlk - cu_ws[dd];
-    const size_t krow = ((size_t)(st.gb * kBlk + 32 * wave + l32) * kHKV + i) * kD + 8 * h;
+    // row fragments: lane (key 32 wave + l32, dims 16 ks + 8 h ..), 1 KB per k-step
+    const size_t kfr = ((size_t)i * NB + st.gb) * kFragBlock + (wave * 8 * 64 + lane) * 8;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      st.kf[ks] = *(const bf16x8 *)(Kw + krow + 16 * ks);
-      st.vf[ks] = *(const bf16x8 *)(Vw + krow + 16 * ks);
+      st.kf[ks] = *(const bf16x8 *)(Kw + kfr + ks * 512);
+      st.vf[ks] = *(const bf16x8 *)(Vw + kfr + ks * 512);
     }
 #pragma unroll
     for (int nd = 0; nd < 4; ++nd)

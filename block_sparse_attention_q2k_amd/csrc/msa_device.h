@@ -20,6 +20,21 @@ constexpr int kTasksHeaderWords = 64;
 constexpr int kPlanHeaderWords = 16;
 constexpr int kPlanMaxList = kFwdGroup * kTopk;  // walk-list capacity per plan item
 constexpr float kLog2e = 1.4426950408889634f;
+// Workspace K/V copies are stored per (KV head kv, workspace block gb) as 16384 bf16
+// (32 KB) at element offset (kv * NB + gb) * kFragBlock, in the order the MFMA operands
+// are loaded, so that every 16-byte-per-lane load of a wave reads 1 KB of contiguous
+// memory:
+//   row fragments (K, V as 32x32x16 A operands, 4 waves x 32 keys): element (key k,
+//     dim d) at ((k/32 * 8 + d/16) * 64 + (d/8 % 2) * 32 + k%32) * 8 + d%8
+//   transposed fragments (K^T, V^T as 16x16x32 A operands, 16-dim slices): element
+//     (key k, dim d) at ((d/16 * 4 + k/32) * 64 + (k/8 % 4) * 16 + d%16) * 8 + k%8
+constexpr int kFragBlock = kBlk * kD;
+__host__ __device__ inline int frag_row_off(int k, int d) {
+  return (((k >> 5) * 8 + (d >> 4)) * 64 + ((d >> 3) & 1) * 32 + (k & 31)) * 8 + (d & 7);
+}
+__host__ __device__ inline int frag_t_off(int k, int d) {
+  return (((d >> 4) * 4 + (k >> 5)) * 64 + ((k >> 3) & 3) * 16 + (d & 15)) * 8 + (k & 7);
+}
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

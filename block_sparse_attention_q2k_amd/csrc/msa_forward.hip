@@ -52,30 +52,30 @@ struct FwdCtx {
   float *sM, *sLw;  // references [unit][head]; row sums [wave][lane half][unit][head]
 };
 
+// Workspace block index (KV head, block) of the item's block b.
+__device__ __forceinline__ size_t fwd_gblk(const FwdCtx &x, int b) {
+  return (size_t)x.i * x.NB + (size_t)(x.wsrow0 / kBlk + b);
+}
+
 __device__ __forceinline__ void fwd_load_k(const FwdCtx &x, bf16x8 (&k)[8], int b) {
-  load_key_rows(k, x.Kw, (size_t)x.wsrow0 + (size_t)b * kBlk, x.i, x.w);
+  load_key_rows(k, x.Kw, fwd_gblk(x, b), x.w);
 }
 
 // Half H (dims 64 H .. + 63) of the K rows of block b: k[4 H .. 4 H + 3].
 template <int H>
 __device__ __forceinline__ void fwd_load_k_half(const FwdCtx &x, bf16x8 (&k)[8], int b) {
-  const uint16_t *row =
-      x.Kw + (((size_t)x.wsrow0 + (size_t)b * kBlk + 32 * x.w.wave + x.w.l32) * kHKV + x.i) * kD + 8 * x.w.hi;
-#pragma unroll
-  for (int ks = 4 * H; ks < 4 * H + 4; ++ks) k[ks] = *(const bf16x8 *)(row + 16 * ks);
+  load_key_rows_half<H>(k, x.Kw, fwd_gblk(x, b), x.w);
 }
 
 __device__ __forceinline__ void fwd_load_v(const FwdCtx &x, bf16x8 (&v)[2][4], int b) {
-  const size_t gblk = (size_t)x.i * x.NB + (size_t)(x.wsrow0 / kBlk + b);
 #pragma unroll
-  for (int md = 0; md < 2; ++md) load_tslice(v[md], x.Vt, gblk, 32 * x.w.wave + 16 * md, x.w.l16, x.w.g);
+  for (int md = 0; md < 2; ++md) load_tslice(v[md], x.Vt, fwd_gblk(x, b), 32 * x.w.wave + 16 * md, x.w);
 }
 
 // V^T slice md (dims 32 w + 16 md ..) of block b.
 template <int MD>
 __device__ __forceinline__ void fwd_load_v_half(const FwdCtx &x, bf16x8 (&v)[2][4], int b) {
-  const size_t gblk = (size_t)x.i * x.NB + (size_t)(x.wsrow0 / kBlk + b);
-  load_tslice(v[MD], x.Vt, gblk, 32 * x.w.wave + 16 * MD, x.w.l16, x.w.g);
+  load_tslice(v[MD], x.Vt, fwd_gblk(x, b), 32 * x.w.wave + 16 * MD, x.w);
 }
 
 // Whether the step's block is the diagonal block of one of the pair's units (uniform;

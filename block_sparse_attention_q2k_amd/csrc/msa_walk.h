@@ -123,22 +123,32 @@ __device__ __forceinline__ void rows_to_lds(char *dst, const char *src, size_t u
   }
 }
 
-// A operand of a 32 x 32 tile: key rows 32w + l32 of a block (workspace X, KV head kv,
-// block starting at workspace row row0), dims 16 ks + 8 hi .. + 7.
-__device__ __forceinline__ void load_key_rows(bf16x8 (&k)[8], const uint16_t *__restrict__ X, size_t row0,
-                                              int kv, const WalkLane &w) {
-  const uint16_t *row = X + ((row0 + 32 * w.wave + w.l32) * kHKV + kv) * kD + 8 * w.hi;
+// A operand of a 32 x 32 tile: key rows 32w + l32 of workspace block gblk (= kv * NB +
+// block) of the row-fragment copy X, dims 16 ks + 8 hi .. + 7: one contiguous 1 KB per
+// k-step.
+__device__ __forceinline__ void load_key_rows(bf16x8 (&k)[8], const uint16_t *__restrict__ X, size_t gblk,
+                                              const WalkLane &w) {
+  const uint16_t *f = X + gblk * kFragBlock + (w.wave * 8 * 64 + w.lane) * 8;
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) k[ks] = *(const bf16x8 *)(row + 16 * ks);
+  for (int ks = 0; ks < 8; ++ks) k[ks] = *(const bf16x8 *)(f + ks * 512);
 }
 
-// A operand of the 16x16x32 products from a transposed block copy Xt[kv][gb][dim][key]:
-// lane (dim dim0 + l16, g) gets keys 32 kk + 8 g + 0..7.
-__device__ __forceinline__ void load_tslice(bf16x8 (&f)[4], const uint16_t *__restrict__ Xt,
-                                            size_t gblk, int dim0, int l16, int g) {
-  const uint16_t *row = Xt + (gblk * kD + dim0 + l16) * kBlk + 8 * g;
+// Half H (k-steps 4 H .. 4 H + 3) of load_key_rows.
+template <int H>
+__device__ __forceinline__ void load_key_rows_half(bf16x8 (&k)[8], const uint16_t *__restrict__ X, size_t gblk,
+                                                   const WalkLane &w) {
+  const uint16_t *f = X + gblk * kFragBlock + (w.wave * 8 * 64 + w.lane) * 8;
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) f[kk] = *(const bf16x8 *)(row + 32 * kk);
+  for (int ks = 4 * H; ks < 4 * H + 4; ++ks) k[ks] = *(const bf16x8 *)(f + ks * 512);
+}
+
+// A operand of the 16x16x32 products from the transposed-fragment copy Xt: lane (dim
+// dim0 + l16, g) gets keys 32 kk + 8 g + 0..7 of block gblk (dim0 a multiple of 16).
+__device__ __forceinline__ void load_tslice(bf16x8 (&f)[4], const uint16_t *__restrict__ Xt, size_t gblk,
+                                            int dim0, const WalkLane &w) {
+  const uint16_t *t = Xt + gblk * kFragBlock + ((dim0 >> 4) * 4 * 64 + w.lane) * 8;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) f[kk] = *(const bf16x8 *)(t + kk * 512);
 }
 
 // B operand of a 32 x 32 tile for the pair (u0, u1) from unit rows in LDS (rows_to_lds,

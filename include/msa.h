@@ -122,9 +122,16 @@ int32_t msa_default_grid(void);
  * K/V workspace alignment (pull-request page, Design: K/V workspaces with each
  * document padded to a multiple of 128 tokens; msa_backward_sm100 API page,
  * run_backward: W a positive multiple of 128).
- *   K, V: bf16 [T, 4, 128] compact.  Kw, Vw: bf16 [W, 4, 128]; row cu_ws[d] + p holds
- *   compact row cu[d] + p for p < L_d and zeros after.  Kt, Vt: bf16 [4][W/128][128]
- *   [128], the same blocks transposed: Kt[kv][gb][c][k] = Kw[128 gb + k][kv][c].
+ *   K, V: bf16 [T, 4, 128] compact.  Workspace row cu_ws[d] + p holds compact row
+ *   cu[d] + p for p < L_d and zeros after; block gb = rows 128 gb .. + 127.  Each of
+ *   Kw, Vw, Kt, Vt holds W * 4 * 128 bf16 as [4][W/128] blocks of 16384 (KV head kv,
+ *   block gb at element (kv * W/128 + gb) * 16384), in the order the kernels' matrix-
+ *   core operands are loaded (each wave-wide 16-byte-per-lane load reads 1 KB of
+ *   contiguous memory):
+ *   Kw, Vw (row fragments): element (key k, dim d) of a block at
+ *     ((k/32 * 8 + d/16) * 64 + (d/8 % 2) * 32 + k%32) * 8 + d%8;
+ *   Kt, Vt (transposed fragments): element (key k, dim d) of a block at
+ *     ((d/16 * 4 + k/32) * 64 + (k/8 % 4) * 16 + d%16) * 8 + k%8.
  * --------------------------------------------------------------------------------- */
 int msa_align_kv(const msa_bf16 *K, const msa_bf16 *V, const msa_layout *layout,
                  msa_bf16 *Kw, msa_bf16 *Vw, msa_bf16 *Kt, msa_bf16 *Vt, void *stream);

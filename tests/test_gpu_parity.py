@@ -143,14 +143,18 @@ def test_two_calls_reuse_buffers_and_stay_consistent():
 
 @pytest.mark.parametrize("name", ["uniform_3docs_ragged", "zipf_many_short"])
 def test_workspace_alignment_bit_exact(name):
-    """Kw/Vw hold each document's rows at its 128-aligned workspace offset, zeros in
-    the padding; Kt/Vt hold the same blocks transposed (keys contiguous)."""
+    """Kw/Vw hold each document's key rows at its 128-aligned workspace offset (zeros in
+    the padding), per (KV head, block) in MFMA row-fragment order; Kt/Vt hold the same
+    blocks in transposed-fragment order (the layouts msa.h documents)."""
     cu, q2k, tens = _small(name)
     m, _ = run_gpu(cu, q2k, tens, backward=False)
     for X, Xw, Xt in (("K", m.Kw, m.Kt), ("V", m.Vw, m.Vt)):
-        ref = OR.align_kv(tens[X].view(torch.int16).numpy(), cu)
-        got = Xw.view(torch.int16).cpu().numpy()
-        np.testing.assert_array_equal(got, ref)
+        ref = OR.align_kv(tens[X].view(torch.int16).numpy(), cu)  # [W][kv][dim]
         NB = ref.shape[0] // 128
-        blocks = ref.reshape(NB, 128, 4, 128).transpose(2, 0, 3, 1)  # [kv][gb][dim][key]
-        np.testing.assert_array_equal(Xt.view(torch.int16).cpu().numpy().reshape(4, NB, 128, 128), blocks)
+        blk = ref.reshape(NB, 128, 4, 128).transpose(2, 0, 1, 3)  # [kv][gb][key][dim]
+        # key = 32 w + l32, dim = 16 ks + 8 hi + e  ->  [kv][gb][w][ks][hi][l32][e]
+        rows = blk.reshape(4, NB, 4, 32, 8, 2, 8).transpose(0, 1, 2, 4, 5, 3, 6)
+        np.testing.assert_array_equal(Xw.view(torch.int16).cpu().numpy().reshape(rows.shape), rows)
+        # key = 32 kk + 8 g + e, dim = 16 dq + l16  ->  [kv][gb][dq][kk][g][l16][e]
+        tr = blk.reshape(4, NB, 4, 4, 8, 8, 16).transpose(0, 1, 5, 2, 3, 6, 4)
+        np.testing.assert_array_equal(Xt.view(torch.int16).cpu().numpy().reshape(tr.shape), tr)
