@@ -81,8 +81,8 @@ def cpu_baseline(cfg, budget_tokens):
 # taken on (sha256 over the files below).
 TRAFFIC_SOURCES = ["msa_backward_kv.hip", "msa_backward_dq.hip", "msa_walk.h", "msa_device.h", "msa_launch.h"]
 TRAFFIC_RECORD = {"config": 2, "dq_mode": "recompute",
-                  "sha256": "020bd2d01d0c45f4a83b4d716b82796dfa6cdef49c05a512deac4fc296cc340b",
-                  "bytes": 11723887120}  # read 11.255 GB + written 0.469 GB
+                  "sha256": "ec862dec23f74bef88ad9227656f582ea79da355934f3e018490c1b094b20157",
+                  "bytes": 11133342719}  # read 10.665 GB + written 0.469 GB
 
 
 def sources_digest():
