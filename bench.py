@@ -76,13 +76,14 @@ def cpu_baseline(cfg, budget_tokens):
 
 
 # HBM bytes per launch of the main backward kernels at the headline workload (config 2,
-# dQ recompute), from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by the same counters'
+# dQ from stored dS tiles), from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by the same counters'
 # reading for a plain copy of known size; valid only for the kernel sources they were
 # taken on (sha256 over the files below).
-TRAFFIC_SOURCES = ["msa_backward_kv.hip", "msa_backward_dq.hip", "msa_walk.h", "msa_device.h", "msa_launch.h"]
-TRAFFIC_RECORD = {"config": 2, "dq_mode": "recompute",
-                  "sha256": "ec862dec23f74bef88ad9227656f582ea79da355934f3e018490c1b094b20157",
-                  "bytes": 11133342719}  # read 10.665 GB + written 0.469 GB
+TRAFFIC_SOURCES = ["msa_backward_kv.hip", "msa_backward_dq.hip", "msa_backward_dqs.hip", "msa_walk.h", "msa_device.h",
+                   "msa_launch.h"]
+TRAFFIC_RECORD = {"config": 2, "dq_mode": "stored",
+                  "sha256": "d3b516cb135ad42498210627c90c48b1496d73650c6d2a3d754bc33067b2f4ad",
+                  "bytes": 17157146537}  # read 12.645 GB + written 4.512 GB
 
 
 def sources_digest():
@@ -120,7 +121,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--dq-mode", choices=["recompute", "fp32", "bf16x2"], default="recompute")
+    ap.add_argument("--dq-mode", choices=["stored", "recompute", "fp32", "bf16x2"], default="stored")
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -150,7 +151,8 @@ def main():
     Q, K, V, dO = tens["Q"], tens["K"], tens["V"], tens["dO"]
     q2k_d = torch.from_numpy(q2k).to(dev)
     scale = 1.0 / math.sqrt(128.0)
-    mode = {"recompute": M.DQ_RECOMPUTE, "fp32": M.DQ_ACCUM_FP32, "bf16x2": M.DQ_ACCUM_BF16X2}[args.dq_mode]
+    mode = {"stored": M.DQ_STORED, "recompute": M.DQ_RECOMPUTE, "fp32": M.DQ_ACCUM_FP32,
+            "bf16x2": M.DQ_ACCUM_BF16X2}[args.dq_mode]
     m = M.MSA(cu, grid=args.grid or None, dq_mode=mode, device=dev)
     O = torch.empty_like(Q)
     LSE = torch.empty((T, 64), dtype=torch.float32, device=dev)
@@ -190,15 +192,17 @@ def main():
     M.msa_set_timing_events(None)
     fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
     bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    split = mode in (M.DQ_RECOMPUTE, M.DQ_STORED)  # separate query-parallel dQ kernel
     recompute = mode == M.DQ_RECOMPUTE
     kern_ms = {"fwd": float(np.mean([e[0].elapsed_time(e[1]) for e in kev])),
                "kv": float(np.mean([e[2].elapsed_time(e[3]) for e in kev])),
-               "dq": float(np.mean([e[4].elapsed_time(e[5]) for e in kev])) if recompute else 0.0}
+               "dq": float(np.mean([e[4].elapsed_time(e[5]) for e in kev])) if split else 0.0}
     ms_step = elapsed * 1e3 / args.steps
     total_flops = fwd_flops + bwd_flops
     value = total_flops / (ms_step * 1e-3) / 1e12
-    # Main backward: the KV-parallel kernel and (recompute mode) the query-parallel dQ
-    # kernel, back to back; together they do the backward's algorithmic contractions.
+    # Main backward: the KV-parallel kernel and (stored / recompute modes) the
+    # query-parallel dQ kernel, back to back; together they do the backward's algorithmic
+    # contractions.
     main_ms = kern_ms["kv"] + kern_ms["dq"]
     achieved = bwd_flops / (main_ms * 1e-3) / 1e12
     status = int(m.status[0].item())
@@ -207,15 +211,16 @@ def main():
         {"kernel": "fwd_kernel", "avg_ms": round(kern_ms["fwd"], 4), "algorithmic_tflop": round(2 * unit / 1e12, 4),
          "executed_tflop": round(2 * unit / 1e12, 4),
          "frac_mfma_peak": round(2 * unit / (kern_ms["fwd"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
-        {"kernel": "bwd_kv_kernel" if recompute else "bwd_kernel", "avg_ms": round(kern_ms["kv"], 4),
-         "algorithmic_tflop": round((4 if recompute else 5) * unit / 1e12, 4),
-         "executed_tflop": round((4 if recompute else 5) * unit / 1e12, 4),
-         "frac_mfma_peak": round((4 if recompute else 5) * unit / (kern_ms["kv"] * 1e-3) / 1e12
+        {"kernel": "bwd_kv_kernel" if split else "bwd_kernel", "avg_ms": round(kern_ms["kv"], 4),
+         "algorithmic_tflop": round((4 if split else 5) * unit / 1e12, 4),
+         "executed_tflop": round((4 if split else 5) * unit / 1e12, 4),
+         "frac_mfma_peak": round((4 if split else 5) * unit / (kern_ms["kv"] * 1e-3) / 1e12
                                  / MFMA_BF16_PEAK_TFLOPS, 4)},
     ]
-    if recompute:
-        kernels.append({"kernel": "dq_kernel", "avg_ms": round(kern_ms["dq"], 4),
-                        "algorithmic_tflop": round(unit / 1e12, 4), "executed_tflop": round(3 * unit / 1e12, 4),
+    if split:
+        kernels.append({"kernel": "dq_kernel" if recompute else "dqs_kernel", "avg_ms": round(kern_ms["dq"], 4),
+                        "algorithmic_tflop": round(unit / 1e12, 4),
+                        "executed_tflop": round((3 if recompute else 1) * unit / 1e12, 4),
                         "frac_mfma_peak": round(unit / (kern_ms["dq"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)})
     traffic = recorded_traffic(args.config, args.dq_mode)
 

@@ -58,6 +58,11 @@ int launch_rc(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH; 
 
 size_t round16(size_t b) { return (b + 15) / 16 * 16; }
 
+// Stored dS tiles: T x 4 index heads x 16 slots x (16 heads x 128 keys) bf16.
+size_t ds_store_bytes(const LayoutArgs &L) {
+  return (size_t)L.T * MSA_NUM_INDEX_HEADS * MSA_TOPK * 16 * MSA_BLOCK * 2;
+}
+
 thread_local hipEvent_t t_events[MSA_TIMING_EVENTS] = {};
 
 // Records timing event k on s if the hook is set.
@@ -121,11 +126,13 @@ size_t msa_bwd_scratch_bytes(const msa_layout *layout, int dq_accum_mode) {
     case MSA_DQ_ACCUM_FP32: elem = 4; break;
     case MSA_DQ_ACCUM_BF16X2: elem = 2; break;
     case MSA_DQ_RECOMPUTE: elem = 0; break;
+    case MSA_DQ_STORED: elem = 0; break;
     default: return 0;
   }
   size_t dq = round16((size_t)L.T * MSA_NUM_Q_HEADS * MSA_HEAD_DIM * elem);
   size_t kv = round16((size_t)L.W * MSA_NUM_KV_HEADS * MSA_HEAD_DIM * 4);
-  return dq + 2 * kv;
+  size_t ds = dq_accum_mode == MSA_DQ_STORED ? ds_store_bytes(L) : 0;
+  return dq + 2 * kv + ds;
 }
 
 int32_t msa_default_grid(void) {
@@ -217,19 +224,23 @@ int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, cons
   if (rc) return rc;
   if (grid < 1 || grid > MSA_MAX_GRID) return MSA_ERR_GRID;
   if (dq_accum_mode != MSA_DQ_ACCUM_FP32 && dq_accum_mode != MSA_DQ_ACCUM_BF16X2 &&
-      dq_accum_mode != MSA_DQ_RECOMPUTE)
+      dq_accum_mode != MSA_DQ_RECOMPUTE && dq_accum_mode != MSA_DQ_STORED)
     return MSA_ERR_MODE;
   if (!(scale > 0.f) || scale != scale) return MSA_ERR_SHAPE;
   if (scratch_bytes < msa_bwd_scratch_bytes(layout, dq_accum_mode)) return MSA_ERR_SCRATCH;
   if ((rc = check_device())) return rc;
   hipStream_t s = (hipStream_t)stream;
-  const bool pool = dq_accum_mode != MSA_DQ_RECOMPUTE;
+  const bool pool = dq_accum_mode == MSA_DQ_ACCUM_FP32 || dq_accum_mode == MSA_DQ_ACCUM_BF16X2;
+  const bool stored = dq_accum_mode == MSA_DQ_STORED;
   size_t elem = dq_accum_mode == MSA_DQ_ACCUM_FP32 ? 4 : (pool ? 2 : 0);
   size_t dq_bytes = round16((size_t)L.T * MSA_NUM_Q_HEADS * MSA_HEAD_DIM * elem);
   size_t kv_bytes = round16((size_t)L.W * MSA_NUM_KV_HEADS * MSA_HEAD_DIM * 4);
+  // scratch: [dQ pool (pooled modes)] [dK pool] [dV pool] [dS tiles (stored mode)]; only
+  // the pools are zeroed (every stored tile is written before it is read)
   char *sc = (char *)scratch;
   float *dk_pool = (float *)(sc + dq_bytes);
   float *dv_pool = (float *)(sc + dq_bytes + kv_bytes);
+  void *ds = stored ? (void *)(sc + dq_bytes + 2 * kv_bytes) : nullptr;
   hipError_t e = host::fill_u32(sc, (dq_bytes + 2 * kv_bytes) / 4, 0u, s);
   if (e == hipSuccess) e = mark(2, s);
   if (e == hipSuccess) {
@@ -237,12 +248,15 @@ int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, cons
       e = host::backward_main(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dq_accum_mode, sc,
                               dk_pool, dv_pool, s);
     else
-      e = host::backward_kv(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dk_pool, dv_pool, s);
+      e = host::backward_kv(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dk_pool, dv_pool, ds,
+                            stored ? q2k : nullptr, s);
   }
   if (e == hipSuccess) e = mark(3, s);
   if (!pool) {
     if (e == hipSuccess) e = mark(4, s);
-    if (e == hipSuccess) e = host::backward_dq(Q, dO, Kw, Vw, Kt, LSE, delta, q2k, L, plan, scale, dQ, s);
+    if (e == hipSuccess)
+      e = stored ? host::backward_dqs(ds, Kt, q2k, L, plan, scale, dQ, s)
+                 : host::backward_dq(Q, dO, Kw, Vw, Kt, LSE, delta, q2k, L, plan, scale, dQ, s);
     if (e == hipSuccess) e = mark(5, s);
   }
   if (e == hipSuccess)

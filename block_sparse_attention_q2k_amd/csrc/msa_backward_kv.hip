@@ -25,7 +25,8 @@ namespace msa {
 
 constexpr int kKvThreads = 256;
 constexpr int kKvTile = 65536;               // Q tile 32 KB + dO tile 32 KB
-constexpr int kKvScalBytes = 3 * 128 * 4;    // lse2[128], delta[128], qpos[128]
+constexpr int kKvScalBytes = 3 * 128 * 4 + 32;  // lse2[128], delta[128], qpos[128], dS tile[8]
+constexpr int kKvScTile = 384;                  // word offset of the dS tile indices
 
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
@@ -111,9 +112,30 @@ struct KvState {
   int pos;
 };
 
+// Stored dS tile index (t * 4 + i) * 16 + j of the queries t of task row `row` (nv valid
+// queries) for block bl (document-local), j = the first member slot of t listing bl;
+// threads tid < 128 (query tid / 16, slot tid % 16).  Waves 0 and 1 each cover 4
+// queries; lane 16 k' of a wave writes query 4 w + k''s index.  The query id is read
+// from the task table per lane (a select over the row's uniform ids would make the
+// compiler keep them in scratch memory).
+__device__ __forceinline__ void kv_member_slots(const int32_t *__restrict__ q2k, int T, int i,
+                                                const int32_t *__restrict__ qrows, int row, int nv, int bl,
+                                                float *sc, int tid) {
+  const int k = tid >> 4, jj = tid & 15;
+  const int t = qrows[(size_t)row * kTileQ + (k < nv ? k : 0)];
+  const bool hit = q2k[((size_t)i * T + t) * kTopk + jj] == bl;
+  const uint64_t ball = __ballot(hit);
+  if (jj == 0) {
+    const uint32_t bits = (uint32_t)(ball >> (16 * ((tid & 63) >> 4))) & 0xFFFFu;
+    ((int32_t *)sc)[kKvScTile + k] = (t * kHI + i) * kTopk + (bits ? __builtin_ctz(bits) : 0);
+  }
+}
+
 // One task row: compute from tile `cur` (+ its scalars), prefetch row + 1 into `nxt`.
+template <bool STORE_DS>
 __device__ __forceinline__ void kv_row(
     KvState &st, int row, int hi, int i, char *cur, float *cur_sc, char *nxt, float *nxt_sc,
+    uint16_t *__restrict__ dS, const int32_t *__restrict__ q2k, int T,
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw, const uint16_t *__restrict__ Vw,
     const uint16_t *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
     const i32x4 *__restrict__ meta, const int32_t *__restrict__ qrows,
@@ -154,12 +176,23 @@ __device__ __forceinline__ void kv_row(
   if (more) {
     kv_row_ids(ids, qrows, qpos, row + 1, meta[row + 1][1]);
     if (tid < 128) kv_scalars(LSE, Delta, ids, i, tid, st.lse2, st.del, st.pos);
+    if (STORE_DS && tid < 128) {
+      // document-local block of row + 1 (usually this row's bucket)
+      const int rn = meta[row + 1][0];
+      int kb = st.kbase;
+      if (rn != r) {
+        const int gbn = rn - i * NB;
+        kb = gbn * kBlk - cu_ws[upper_index(cu_ws, ndocs - 1, gbn * kBlk)];
+      }
+      kv_member_slots(q2k, T, i, qrows, row + 1, meta[row + 1][1], kb / kBlk, nxt_sc, tid);
+    }
   }
   // 3. compute
   const int kp = st.kbase + 32 * wave + l32;  // document-local position of this lane's key
 #pragma unroll 1
   for (int half = 0; half < 2; ++half) {
     if (more) kv_gather_part<0>(Q, dO, ids, i, nxt, tid, half);
+    const i32x4 tix = STORE_DS ? *(const i32x4 *)((const int32_t *)cur_sc + kKvScTile + 4 * half) : i32x4{};
     f32x16 sacc[2], pacc[2];
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2) {
@@ -202,6 +235,14 @@ __device__ __forceinline__ void kv_row(
         pa[e] = (__bf16)sacc[m2][8 * sg + e];
         sa[e] = (__bf16)pacc[m2][8 * sg + e];
       }
+      if (STORE_DS && 4 * half + k2 < mt4[1]) {
+        // sa: query 4 half + k2, key 32 w + l32, heads 4 h .. + 3 and 8 + 4 h .. + 3,
+        // which are tile positions 8 h .. 8 h + 7.  Streaming (non-temporal) store: the
+        // tiles are read once, by the dQ kernel, and should not displace the Q/dO rows
+        // the gathers re-read from the caches.
+        const size_t tile = (size_t)__builtin_amdgcn_readfirstlane(tix[k2]) * (kBlk * 16);
+        __builtin_nontemporal_store(sa, (bf16x8 *)(dS + tile + ds_key_swz(32 * wave + l32) * 16 + 8 * h));
+      }
 #pragma unroll
       for (int nd = 0; nd < 4; ++nd) {
         // B: lane (dim 32nd + l32, h) holds rows 16ks + 4h + 0..3 and 16ks + 8 + 4h + 0..3
@@ -236,8 +277,10 @@ __device__ __forceinline__ void kv_row(
   __syncthreads();
 }
 
+template <bool STORE_DS>
 __global__ void __launch_bounds__(kKvThreads, 1)
-bwd_kv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
+bwd_kv_kernel(uint16_t *__restrict__ dS, const int32_t *__restrict__ q2k, int T,
+              const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
               const uint16_t *__restrict__ Vw, const uint16_t *__restrict__ dO,
               const float *__restrict__ LSE, const float *__restrict__ Delta,
               const int32_t *__restrict__ cta, const i32x4 *__restrict__ meta,
@@ -261,6 +304,11 @@ bwd_kv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
       if (tid < 128) {
         kv_scalars(LSE, Delta, ids, i, tid, st.lse2, st.del, st.pos);
         kv_store_scalars(sc0, tid, st.lse2, st.del, st.pos);
+        if (STORE_DS) {
+          const int gb0 = meta[lo][0] - i * NB;
+          const int kb0 = gb0 * kBlk - cu_ws[upper_index(cu_ws, ndocs - 1, gb0 * kBlk)];
+          kv_member_slots(q2k, T, i, qrows, lo, meta[lo][1], kb0 / kBlk, sc0, tid);
+        }
       }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -272,11 +320,11 @@ bwd_kv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
     }
     st.cur_r = -1;
     for (int row = lo; row < hi; row += 2) {
-      kv_row(st, row, hi, i, tile0, sc0, tile1, sc1, Q, Kw, Vw, dO, LSE, Delta, meta, qrows, qpos,
-             cu_ws, ndocs, NB, scale, scale_log2e, dk_pool, dv_pool, tid);
+      kv_row<STORE_DS>(st, row, hi, i, tile0, sc0, tile1, sc1, dS, q2k, T, Q, Kw, Vw, dO, LSE, Delta, meta,
+                       qrows, qpos, cu_ws, ndocs, NB, scale, scale_log2e, dk_pool, dv_pool, tid);
       if (row + 1 < hi)
-        kv_row(st, row + 1, hi, i, tile1, sc1, tile0, sc0, Q, Kw, Vw, dO, LSE, Delta, meta, qrows,
-               qpos, cu_ws, ndocs, NB, scale, scale_log2e, dk_pool, dv_pool, tid);
+        kv_row<STORE_DS>(st, row + 1, hi, i, tile1, sc1, tile0, sc0, dS, q2k, T, Q, Kw, Vw, dO, LSE, Delta,
+                         meta, qrows, qpos, cu_ws, ndocs, NB, scale, scale_log2e, dk_pool, dv_pool, tid);
     }
   }
 }
@@ -285,9 +333,10 @@ namespace host {
 hipError_t backward_kv(const void *Q, const void *Kw, const void *Vw, const void *dO,
                        const float *LSE, const float *delta, const void *tasks,
                        const LayoutArgs &L, int grid, float scale, float *dk_pool, float *dv_pool,
-                       hipStream_t s) {
+                       void *dS, const int32_t *q2k, hipStream_t s) {
   TaskView v = task_view(L, grid, const_cast<void *>(tasks));
-  hipLaunchKernelGGL(bwd_kv_kernel, dim3(grid), dim3(kKvThreads), 0, s, (const uint16_t *)Q,
+  auto kern = dS ? bwd_kv_kernel<true> : bwd_kv_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kKvThreads), 0, s, (uint16_t *)dS, q2k, L.T, (const uint16_t *)Q,
                      (const uint16_t *)Kw, (const uint16_t *)Vw, (const uint16_t *)dO, LSE, delta,
                      v.cta, (const i32x4 *)v.meta, v.qrows, v.qpos, L.cu_ws, L.ndocs, L.NB, grid,
                      scale, scale * kLog2e, dk_pool, dv_pool);

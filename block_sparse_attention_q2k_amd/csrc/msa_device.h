@@ -29,6 +29,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 //   transposed fragments (K^T, V^T as 16x16x32 A operands, 16-dim slices): element
 //     (key k, dim d) at ((d/16 * 4 + k/32) * 64 + (k/8 % 4) * 16 + d%16) * 8 + k%8
 constexpr int kFragBlock = kBlk * kD;
+// Stored dS tiles (MSA_DQ_STORED): the dS values of one (query t, index head i, member
+// slot j) -- 16 heads x 128 keys of the block q2k[i][t][j] -- as 2048 bf16 at tile
+// (t * 4 + i) * 16 + j, element (key, head) at ds_key_swz(key) * 16 + ds_head_pos(head).
+// key' = key ^ (key / 8 % 2) * 4: within every 16 keys the second 8 swap their 4-key
+// quarters, which spreads the dQ kernel's transposing LDS reads over all banks.  Head
+// positions swap bits 2 and 3 (order 0-3, 8-11, 4-7, 12-15): the 8 heads one lane of
+// the KV-parallel kernel holds for a key are then 16 contiguous bytes.
+__host__ __device__ inline int ds_key_swz(int key) { return key ^ (((key >> 3) & 1) << 2); }
+__host__ __device__ inline int ds_head_pos(int h) { return (h & 3) | ((h & 4) << 1) | ((h & 8) >> 1); }
 __host__ __device__ inline int frag_row_off(int k, int d) {
   return (((k >> 5) * 8 + (d >> 4)) * 64 + ((d >> 3) & 1) * 32 + (k & 31)) * 8 + (d & 7);
 }

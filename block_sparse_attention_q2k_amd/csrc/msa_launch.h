@@ -46,10 +46,13 @@ hipError_t backward_main(const void *Q, const void *Kw, const void *Vw, const vo
                          const float *LSE, const float *delta, const void *tasks,
                          const LayoutArgs &L, int grid, float scale, int mode, void *dq_pool,
                          float *dk_pool, float *dv_pool, hipStream_t s);
+// dS / q2k non-null: also store the dS tiles (MSA_DQ_STORED).
 hipError_t backward_kv(const void *Q, const void *Kw, const void *Vw, const void *dO,
                        const float *LSE, const float *delta, const void *tasks,
                        const LayoutArgs &L, int grid, float scale, float *dk_pool, float *dv_pool,
-                       hipStream_t s);
+                       void *dS, const int32_t *q2k, hipStream_t s);
+hipError_t backward_dqs(const void *dS, const void *Kt, const int32_t *q2k, const LayoutArgs &L,
+                        const void *plan, float scale, void *dQ, hipStream_t s);
 hipError_t backward_dq(const void *Q, const void *dO, const void *Kw, const void *Vw, const void *Kt,
                        const float *LSE, const float *delta, const int32_t *q2k, const LayoutArgs &L,
                        const void *plan, float scale, void *dQ, hipStream_t s);

@@ -73,9 +73,14 @@ enum {
  * modes FP32 and BF16X2 do that (fp32 atomics / packed bf16 pair atomics from the
  * KV-parallel kernel, then a cast).  MSA_DQ_RECOMPUTE instead computes dQ in a
  * query-parallel kernel that recomputes P and dS per selected block and stores dQ
- * directly (no pool, no atomics); it is the fastest on gfx950, where global atomic
- * throughput, not the matrix cores, bounds the pooled modes. */
-enum { MSA_DQ_ACCUM_FP32 = 0, MSA_DQ_ACCUM_BF16X2 = 1, MSA_DQ_RECOMPUTE = 2 };
+ * directly (no pool, no atomics); on gfx950 global atomic throughput, not the matrix
+ * cores, bounds the pooled modes.  MSA_DQ_STORED has the KV-parallel kernel, which forms
+ * every dS value anyway, store each (query, index head, member slot) dS tile (bf16,
+ * 4 KiB) in the scratch, and a query-parallel kernel contract them with K: no
+ * recomputation and no atomics, at 4 KiB x 16 x 4 = 256 KiB of scratch per token; the
+ * fastest, and the default of the Python binding.  Modes differ in rounding only (dS is
+ * rounded to bf16 before its products in all of them). */
+enum { MSA_DQ_ACCUM_FP32 = 0, MSA_DQ_ACCUM_BF16X2 = 1, MSA_DQ_RECOMPUTE = 2, MSA_DQ_STORED = 3 };
 
 #define MSA_MAX_GRID 4096
 

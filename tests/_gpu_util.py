@@ -56,7 +56,7 @@ def check_lse(gpu, ref, mask=None):
     return check_close("LSE", g[~ninf], r[~ninf])
 
 
-def run_gpu(cu, q2k, tens, mode=2, grid=None, backward=True):
+def run_gpu(cu, q2k, tens, mode=3, grid=None, backward=True):
     """Forward (+ backward) of the HIP path on cuda:0.  Returns (msa object, outputs)."""
     M = msa_module()
     dev = "cuda:0"

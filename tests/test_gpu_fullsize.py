@@ -73,7 +73,7 @@ def _case(cfg):
     return cu, q2k, tens, qmask, kmask, ref
 
 
-@pytest.mark.parametrize("mode", [2, 0])
+@pytest.mark.parametrize("mode", [3, 2])
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_full_size_config(cfg, mode):
     say("config", cfg, "dq mode", mode)

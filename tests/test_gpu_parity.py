@@ -52,7 +52,7 @@ def test_forward_parity_small(name):
     check_lse(to_np(out["LSE"]), LSE)
 
 
-@pytest.mark.parametrize("mode", [2, 0, 1])
+@pytest.mark.parametrize("mode", [3, 2, 0, 1])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_backward_parity_small(name, mode):
     say("case", name, "dq mode", mode)
@@ -115,7 +115,7 @@ def test_forward_reference_fallback_rows():
     Q[300:310] = 96.0 * u
     K[128:132] = 16.0 * u
     tens = dict(tens, Q=Q.to(torch.bfloat16), K=K.to(torch.bfloat16))
-    m, out = run_gpu(cu, q2k, tens, mode=2)
+    m, out = run_gpu(cu, q2k, tens, mode=3)
     Q64, K64, V64, dO64 = inputs64(tens)
     O, LSE = OR.forward(Q64, K64, V64, q2k, cu, SCALE)
     check_close("O", to_np(out["O"]), O)
