@@ -72,7 +72,7 @@ def lib():
             "msa_forward": (I, [P, P, P, P, LP, P, F, P, P, P]),
             "msa_backward_preprocess": (I, [P, P, I, P, P]),
             "msa_tasks_meta_offset": (Z, [I]),
-            "msa_build_tasks": (I, [LP, P, P, I, P, Z, P]),
+            "msa_build_tasks": (I, [LP, P, P, P, I, P, Z, P]),
             "msa_backward": (I, [P, P, P, P, P, P, P, P, P, P, I, LP, F, I, P, P, P, P, Z, P]),
             "msa_status_string": (ctypes.c_char_p, [I]),
             "msa_set_timing_events": (None, [P]),
@@ -184,9 +184,9 @@ def msa_backward_preprocess(O, dO, num_tokens, delta, stream=None):
         _ptr(O), _ptr(dO), int(num_tokens), _ptr(delta), _stream(stream)))
 
 
-def msa_build_tasks(layout, row_ptr, cols, grid, tasks, stream=None):
-    _check("msa_build_tasks", lib().msa_build_tasks(layout.ref(), _ptr(row_ptr), _ptr(cols), int(grid),
-                                                    _ptr(tasks), tasks.numel() * tasks.element_size(),
+def msa_build_tasks(layout, row_ptr, cols, q2k, grid, tasks, stream=None):
+    _check("msa_build_tasks", lib().msa_build_tasks(layout.ref(), _ptr(row_ptr), _ptr(cols), _ptr(q2k),
+                                                    int(grid), _ptr(tasks), tasks.numel() * tasks.element_size(),
                                                     _stream(stream)))
 
 
@@ -268,7 +268,7 @@ class MSA:
         if dV is None:
             dV = torch.empty_like(dK)
         msa_backward_preprocess(O, dO, L.T, self.delta, stream)
-        msa_build_tasks(L, self.row_ptr, self.cols, self.grid, self.tasks, stream)
+        msa_build_tasks(L, self.row_ptr, self.cols, self.q2k, self.grid, self.tasks, stream)
         msa_backward(Q, self.Kw, self.Vw, self.Kt, dO, LSE, self.delta, self.q2k, self.plan,
                      self.tasks, self.grid, L, scale, self.dq_mode, dQ, dK, dV, self.bwd_scratch,
                      stream)
@@ -300,9 +300,10 @@ class MSA:
         meta = w[mo: mo + 4 * rmax].reshape(-1, 4)[:R]
         qrows = w[mo + 4 * rmax: mo + 12 * rmax].reshape(-1, 8)[:R]
         qpos = w[mo + 12 * rmax: mo + 20 * rmax].reshape(-1, 8)[:R]
+        qtile = w[mo + 20 * rmax: mo + 28 * rmax].reshape(-1, 8)[:R]
         cta = w[TASKS_HEADER_WORDS: TASKS_HEADER_WORDS + 4 * (grid + 1)].reshape(4, grid + 1)
         return dict(R=R, head_rows=w[1:5].copy(), head_first=w[5:9].copy(), grid=grid, meta=meta,
-                    qrows=qrows, qpos=qpos, cta=cta)
+                    qrows=qrows, qpos=qpos, qtile=qtile, cta=cta)
 
 
 def torch_int32():

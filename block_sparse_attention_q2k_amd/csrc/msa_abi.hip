@@ -202,15 +202,15 @@ int msa_backward_preprocess(const msa_bf16 *O, const msa_bf16 *dO, int32_t num_t
 }
 
 int msa_build_tasks(const msa_layout *layout, const int32_t *row_ptr, const int32_t *cols,
-                    int32_t grid, void *tasks, size_t tasks_bytes, void *stream) {
+                    const int32_t *q2k, int32_t grid, void *tasks, size_t tasks_bytes, void *stream) {
   LayoutArgs L;
   int rc = check_layout(layout, &L);
-  if (!rc) rc = check_ptrs({row_ptr, cols, tasks});
+  if (!rc) rc = check_ptrs({row_ptr, cols, q2k, tasks});
   if (rc) return rc;
   if (grid < 1 || grid > MSA_MAX_GRID) return MSA_ERR_GRID;
   if (tasks_bytes < msa_tasks_bytes(layout, grid)) return MSA_ERR_SCRATCH;
   if ((rc = check_device())) return rc;
-  return launch_rc(host::build_tasks(L, row_ptr, cols, grid, tasks, (hipStream_t)stream));
+  return launch_rc(host::build_tasks(L, row_ptr, cols, q2k, grid, tasks, (hipStream_t)stream));
 }
 
 int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, const msa_bf16 *Kt,
@@ -248,8 +248,7 @@ int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, cons
       e = host::backward_main(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dq_accum_mode, sc,
                               dk_pool, dv_pool, s);
     else
-      e = host::backward_kv(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dk_pool, dv_pool, ds,
-                            stored ? q2k : nullptr, s);
+      e = host::backward_kv(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dk_pool, dv_pool, ds, s);
   }
   if (e == hipSuccess) e = mark(3, s);
   if (!pool) {

@@ -25,8 +25,8 @@ namespace msa {
 
 constexpr int kKvThreads = 256;
 constexpr int kKvTile = 65536;               // Q tile 32 KB + dO tile 32 KB
-constexpr int kKvScalBytes = 3 * 128 * 4 + 32;  // lse2[128], delta[128], qpos[128], dS tile[8]
-constexpr int kKvScTile = 384;                  // word offset of the dS tile indices
+constexpr int kKvScalBytes = (2 * 128 + 8 + 8) * 4;  // lse2[128], delta[128], qpos[8], dS tile[8]
+constexpr int kKvScPos = 256, kKvScTile = 264;      // word offsets of qpos / dS tile indices
 
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
@@ -77,7 +77,8 @@ __device__ __forceinline__ void kv_gather_part(const uint16_t *__restrict__ Q, c
   }
 }
 
-// Raw per-row scalars for LDS row tid (< 128): LSE, delta and position of query tid/16.
+// Raw per-row scalars for LDS row tid (< 128): LSE, delta and position of query tid/16
+// (-1 for a padding query).
 __device__ __forceinline__ void kv_scalars(const float *__restrict__ LSE, const float *__restrict__ Delta,
                                            const KvRowIds &ids, int i, int tid, float &lse,
                                            float &del, int &pos) {
@@ -98,7 +99,7 @@ __device__ __forceinline__ void kv_scalars(const float *__restrict__ LSE, const 
 __device__ __forceinline__ void kv_store_scalars(float *sc, int tid, float lse, float del, int pos) {
   sc[tid] = lse * kLog2e;
   sc[128 + tid] = del;
-  ((int32_t *)sc)[256 + tid] = pos;
+  if ((tid & 15) == 0) ((int32_t *)sc)[kKvScPos + (tid >> 4)] = pos;
 }
 
 // s_waitcnt vmcnt(0) in a form the compiler's wait-count tracking understands
@@ -109,33 +110,14 @@ struct KvState {
   bf16x8 kf[8], vf[8];
   int cur_r, kbase, gb;
   float lse2, del;
-  int pos;
+  int pos, qt;  // qt: stored-dS tile index of the next row's query tid (tid < 8)
 };
-
-// Stored dS tile index (t * 4 + i) * 16 + j of the queries t of task row `row` (nv valid
-// queries) for block bl (document-local), j = the first member slot of t listing bl;
-// threads tid < 128 (query tid / 16, slot tid % 16).  Waves 0 and 1 each cover 4
-// queries; lane 16 k' of a wave writes query 4 w + k''s index.  The query id is read
-// from the task table per lane (a select over the row's uniform ids would make the
-// compiler keep them in scratch memory).
-__device__ __forceinline__ void kv_member_slots(const int32_t *__restrict__ q2k, int T, int i,
-                                                const int32_t *__restrict__ qrows, int row, int nv, int bl,
-                                                float *sc, int tid) {
-  const int k = tid >> 4, jj = tid & 15;
-  const int t = qrows[(size_t)row * kTileQ + (k < nv ? k : 0)];
-  const bool hit = q2k[((size_t)i * T + t) * kTopk + jj] == bl;
-  const uint64_t ball = __ballot(hit);
-  if (jj == 0) {
-    const uint32_t bits = (uint32_t)(ball >> (16 * ((tid & 63) >> 4))) & 0xFFFFu;
-    ((int32_t *)sc)[kKvScTile + k] = (t * kHI + i) * kTopk + (bits ? __builtin_ctz(bits) : 0);
-  }
-}
 
 // One task row: compute from tile `cur` (+ its scalars), prefetch row + 1 into `nxt`.
 template <bool STORE_DS>
 __device__ __forceinline__ void kv_row(
     KvState &st, int row, int hi, int i, char *cur, float *cur_sc, char *nxt, float *nxt_sc,
-    uint16_t *__restrict__ dS, const int32_t *__restrict__ q2k, int T,
+    uint16_t *__restrict__ dS, const int32_t *__restrict__ qtile,
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw, const uint16_t *__restrict__ Vw,
     const uint16_t *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
     const i32x4 *__restrict__ meta, const int32_t *__restrict__ qrows,
@@ -176,19 +158,18 @@ __device__ __forceinline__ void kv_row(
   if (more) {
     kv_row_ids(ids, qrows, qpos, row + 1, meta[row + 1][1]);
     if (tid < 128) kv_scalars(LSE, Delta, ids, i, tid, st.lse2, st.del, st.pos);
-    if (STORE_DS && tid < 128) {
-      // document-local block of row + 1 (usually this row's bucket)
-      const int rn = meta[row + 1][0];
-      int kb = st.kbase;
-      if (rn != r) {
-        const int gbn = rn - i * NB;
-        kb = gbn * kBlk - cu_ws[upper_index(cu_ws, ndocs - 1, gbn * kBlk)];
-      }
-      kv_member_slots(q2k, T, i, qrows, row + 1, meta[row + 1][1], kb / kBlk, nxt_sc, tid);
-    }
+    if (STORE_DS && tid < kTileQ) st.qt = qtile[(size_t)(row + 1) * kTileQ + tid];
   }
-  // 3. compute
+  // 3. compute.  Causal mask of this lane's key against the row's 8 queries, bit q set
+  //    when query q sees it (never for padding queries, whose position is -1).
   const int kp = st.kbase + 32 * wave + l32;  // document-local position of this lane's key
+  uint32_t vis = 0;
+  {
+    const i32x4 pa = *(const i32x4 *)((const int32_t *)cur_sc + kKvScPos);
+    const i32x4 pb = *(const i32x4 *)((const int32_t *)cur_sc + kKvScPos + 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) vis |= (kp <= pa[q] ? 1u : 0u) << q | (kp <= pb[q] ? 16u : 0u) << q;
+  }
 #pragma unroll 1
   for (int half = 0; half < 2; ++half) {
     if (more) kv_gather_part<0>(Q, dO, ids, i, nxt, tid, half);
@@ -207,7 +188,8 @@ __device__ __forceinline__ void kv_row(
       }
     }
     if (more) kv_gather_part<2>(Q, dO, ids, i, nxt, tid, half);
-    // P, dS: register e of sacc[m2] is row 32mt + 8(e/4) + 4h + e%4
+    // P, dS: register e of sacc[m2] is row 32mt + 8(e/4) + 4h + e%4, query 2mt + e/8
+    const uint32_t vh = vis >> (4 * half);
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2) {
       const int mt = 2 * half + m2;
@@ -216,10 +198,10 @@ __device__ __forceinline__ void kv_row(
         const int r0 = 32 * mt + 8 * q4 + 4 * h;
         const f32x4 l4 = *(const f32x4 *)(cur_sc + r0);
         const f32x4 d4 = *(const f32x4 *)(cur_sc + 128 + r0);
-        const i32x4 p4 = *(const i32x4 *)((const int32_t *)cur_sc + 256 + r0);
+        const bool seen = (vh >> (2 * m2 + (q4 >> 1))) & 1u;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float pr = kp <= p4[e] ? __builtin_amdgcn_exp2f(sacc[m2][4 * q4 + e] * scale_log2e - l4[e]) : 0.f;
+          const float pr = seen ? __builtin_amdgcn_exp2f(sacc[m2][4 * q4 + e] * scale_log2e - l4[e]) : 0.f;
           sacc[m2][4 * q4 + e] = pr;
           pacc[m2][4 * q4 + e] = pr * (pacc[m2][4 * q4 + e] - d4[e]);
         }
@@ -273,13 +255,14 @@ __device__ __forceinline__ void kv_row(
   }
   // 5. scalars of row + 1 -> LDS; wait for its gather; everyone done with `cur`
   if (more && tid < 128) kv_store_scalars(nxt_sc, tid, st.lse2, st.del, st.pos);
+  if (STORE_DS && more && tid < kTileQ) ((int32_t *)nxt_sc)[kKvScTile + tid] = st.qt;
   wait_vm();
   __syncthreads();
 }
 
 template <bool STORE_DS>
 __global__ void __launch_bounds__(kKvThreads, 1)
-bwd_kv_kernel(uint16_t *__restrict__ dS, const int32_t *__restrict__ q2k, int T,
+bwd_kv_kernel(uint16_t *__restrict__ dS, const int32_t *__restrict__ qtile,
               const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
               const uint16_t *__restrict__ Vw, const uint16_t *__restrict__ dO,
               const float *__restrict__ LSE, const float *__restrict__ Delta,
@@ -304,11 +287,7 @@ bwd_kv_kernel(uint16_t *__restrict__ dS, const int32_t *__restrict__ q2k, int T,
       if (tid < 128) {
         kv_scalars(LSE, Delta, ids, i, tid, st.lse2, st.del, st.pos);
         kv_store_scalars(sc0, tid, st.lse2, st.del, st.pos);
-        if (STORE_DS) {
-          const int gb0 = meta[lo][0] - i * NB;
-          const int kb0 = gb0 * kBlk - cu_ws[upper_index(cu_ws, ndocs - 1, gb0 * kBlk)];
-          kv_member_slots(q2k, T, i, qrows, lo, meta[lo][1], kb0 / kBlk, sc0, tid);
-        }
+        if (STORE_DS && tid < kTileQ) ((int32_t *)sc0)[kKvScTile + tid] = qtile[(size_t)lo * kTileQ + tid];
       }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -320,10 +299,10 @@ bwd_kv_kernel(uint16_t *__restrict__ dS, const int32_t *__restrict__ q2k, int T,
     }
     st.cur_r = -1;
     for (int row = lo; row < hi; row += 2) {
-      kv_row<STORE_DS>(st, row, hi, i, tile0, sc0, tile1, sc1, dS, q2k, T, Q, Kw, Vw, dO, LSE, Delta, meta,
+      kv_row<STORE_DS>(st, row, hi, i, tile0, sc0, tile1, sc1, dS, qtile, Q, Kw, Vw, dO, LSE, Delta, meta,
                        qrows, qpos, cu_ws, ndocs, NB, scale, scale_log2e, dk_pool, dv_pool, tid);
       if (row + 1 < hi)
-        kv_row<STORE_DS>(st, row + 1, hi, i, tile1, sc1, tile0, sc0, dS, q2k, T, Q, Kw, Vw, dO, LSE, Delta,
+        kv_row<STORE_DS>(st, row + 1, hi, i, tile1, sc1, tile0, sc0, dS, qtile, Q, Kw, Vw, dO, LSE, Delta,
                          meta, qrows, qpos, cu_ws, ndocs, NB, scale, scale_log2e, dk_pool, dv_pool, tid);
     }
   }
@@ -333,10 +312,10 @@ namespace host {
 hipError_t backward_kv(const void *Q, const void *Kw, const void *Vw, const void *dO,
                        const float *LSE, const float *delta, const void *tasks,
                        const LayoutArgs &L, int grid, float scale, float *dk_pool, float *dv_pool,
-                       void *dS, const int32_t *q2k, hipStream_t s) {
+                       void *dS, hipStream_t s) {
   TaskView v = task_view(L, grid, const_cast<void *>(tasks));
   auto kern = dS ? bwd_kv_kernel<true> : bwd_kv_kernel<false>;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kKvThreads), 0, s, (uint16_t *)dS, q2k, L.T, (const uint16_t *)Q,
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kKvThreads), 0, s, (uint16_t *)dS, v.qtile, (const uint16_t *)Q,
                      (const uint16_t *)Kw, (const uint16_t *)Vw, (const uint16_t *)dO, LSE, delta,
                      v.cta, (const i32x4 *)v.meta, v.qrows, v.qpos, L.cu_ws, L.ndocs, L.NB, grid,
                      scale, scale * kLog2e, dk_pool, dv_pool);

@@ -422,12 +422,16 @@ tasks_header_kernel(const int32_t *__restrict__ tile_off, int NB, int grid, int 
   }
 }
 
-// One thread per CSR entry e: row of bucket r, slot (e - row_ptr[r]) % 8.
+// One thread per CSR entry e: row of bucket r, slot (e - row_ptr[r]) % 8.  Also the
+// stored-dS tile index of the entry: (t * 4 + i) * 16 + j, j = the first q2k slot of
+// (i, t) listing the bucket's document-local block.
 __global__ void tasks_fill_kernel(const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ cols,
                                   const int32_t *__restrict__ tile_off,
                                   const int32_t *__restrict__ cu, const int32_t *__restrict__ cu_ws,
+                                  const int32_t *__restrict__ q2k, int T,
                                   int ndocs, int NB, int cap, i32x4 *__restrict__ meta,
-                                  int32_t *__restrict__ qrows, int32_t *__restrict__ qpos) {
+                                  int32_t *__restrict__ qrows, int32_t *__restrict__ qpos,
+                                  int32_t *__restrict__ qtile) {
   int e = blockIdx.x * blockDim.x + threadIdx.x;
   int nrows = kHI * NB;
   if (e >= cap || e >= row_ptr[nrows]) return;
@@ -441,6 +445,13 @@ __global__ void tasks_fill_kernel(const int32_t *__restrict__ row_ptr, const int
   int t = cols[e];
   qrows[(size_t)row * kTileQ + s] = t;
   qpos[(size_t)row * kTileQ + s] = t - cu[d];
+  {
+    const int i = r / NB, bl = gb - cu_ws[d] / kBlk;
+    const int32_t *sel = q2k + ((size_t)i * T + t) * kTopk;
+    int j = 0;
+    while (j < kTopk - 1 && sel[j] != bl) ++j;  // the CSR entry exists, so some slot lists bl
+    qtile[(size_t)row * kTileQ + s] = (t * kHI + i) * kTopk + j;
+  }
   if (s == 0) {
     int len = row_ptr[r + 1] - row_ptr[r];
     int ntile = (len + kTileQ - 1) / kTileQ;
@@ -450,6 +461,7 @@ __global__ void tasks_fill_kernel(const int32_t *__restrict__ row_ptr, const int
     for (int p = nv; p < kTileQ; ++p) {
       qrows[(size_t)row * kTileQ + p] = -1;
       qpos[(size_t)row * kTileQ + p] = -1;
+      qtile[(size_t)row * kTileQ + p] = -1;
     }
   }
 }
@@ -598,7 +610,7 @@ size_t tasks_meta_offset_words(int grid) {
 }
 size_t tasks_bytes(const LayoutArgs &L, int grid) {
   size_t rmax = tasks_rmax(L);
-  size_t words = tasks_meta_offset_words(grid) + 4 * rmax + 2 * kTileQ * rmax  // meta, qrows, qpos
+  size_t words = tasks_meta_offset_words(grid) + 4 * rmax + 3 * kTileQ * rmax  // meta, qrows, qpos, qtile
                  + 2 * ((size_t)kHI * L.NB + 1) + 64;                        // lengths, tile_off
   return words * 4;
 }
@@ -612,14 +624,15 @@ TaskView task_view(const LayoutArgs &L, int grid, void *tasks_v) {
   v.meta = tasks + tasks_meta_offset_words(grid);
   v.qrows = v.meta + 4 * rmax;
   v.qpos = v.qrows + kTileQ * rmax;
-  v.len = v.qpos + kTileQ * rmax;
+  v.qtile = v.qpos + kTileQ * rmax;
+  v.len = v.qtile + kTileQ * rmax;
   v.tile_off = v.len + ((size_t)kHI * L.NB + 1);
   v.rmax = rmax;
   return v;
 }
 
-hipError_t build_tasks(const LayoutArgs &L, const int32_t *row_ptr, const int32_t *cols, int grid,
-                       void *tasks_v, hipStream_t s) {
+hipError_t build_tasks(const LayoutArgs &L, const int32_t *row_ptr, const int32_t *cols,
+                       const int32_t *q2k, int grid, void *tasks_v, hipStream_t s) {
   TaskView v = task_view(L, grid, tasks_v);
   int nrows = kHI * L.NB;
   hipLaunchKernelGGL(row_len_kernel, dim3(blocks_for(nrows, 256)), dim3(256), 0, s, row_ptr, nrows,
@@ -630,8 +643,8 @@ hipError_t build_tasks(const LayoutArgs &L, const int32_t *row_ptr, const int32_
                      (int)v.rmax, v.header);
   size_t cap = (size_t)kHI * L.T * kTopk;
   hipLaunchKernelGGL(tasks_fill_kernel, dim3(blocks_for(cap, 256)), dim3(256), 0, s, row_ptr, cols,
-                     v.tile_off, L.cu, L.cu_ws, L.ndocs, L.NB, (int)cap, (i32x4 *)v.meta, v.qrows,
-                     v.qpos);
+                     v.tile_off, L.cu, L.cu_ws, q2k, L.T, L.ndocs, L.NB, (int)cap, (i32x4 *)v.meta,
+                     v.qrows, v.qpos, v.qtile);
   return hipGetLastError();
 }
 

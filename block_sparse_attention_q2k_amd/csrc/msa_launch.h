@@ -16,7 +16,7 @@ struct PlanView {
 };
 
 struct TaskView {
-  int32_t *header, *cta, *meta, *qrows, *qpos, *len, *tile_off;
+  int32_t *header, *cta, *meta, *qrows, *qpos, *qtile, *len, *tile_off;
   size_t rmax;
 };
 
@@ -34,8 +34,8 @@ size_t tasks_rmax(const LayoutArgs &L);
 size_t tasks_meta_offset_words(int grid);
 size_t tasks_bytes(const LayoutArgs &L, int grid);
 TaskView task_view(const LayoutArgs &L, int grid, void *tasks);
-hipError_t build_tasks(const LayoutArgs &L, const int32_t *row_ptr, const int32_t *cols, int grid,
-                       void *tasks, hipStream_t s);
+hipError_t build_tasks(const LayoutArgs &L, const int32_t *row_ptr, const int32_t *cols,
+                       const int32_t *q2k, int grid, void *tasks, hipStream_t s);
 hipError_t preprocess(const void *O, const void *dO, int T, float *delta, hipStream_t s);
 hipError_t finalize(const void *dq_pool, int mode, const float *dk_pool, const float *dv_pool,
                     const LayoutArgs &L, void *dQ, void *dK, void *dV, hipStream_t s);
@@ -46,11 +46,11 @@ hipError_t backward_main(const void *Q, const void *Kw, const void *Vw, const vo
                          const float *LSE, const float *delta, const void *tasks,
                          const LayoutArgs &L, int grid, float scale, int mode, void *dq_pool,
                          float *dk_pool, float *dv_pool, hipStream_t s);
-// dS / q2k non-null: also store the dS tiles (MSA_DQ_STORED).
+// dS non-null: also store the dS tiles (MSA_DQ_STORED) at the tasks' tile indices.
 hipError_t backward_kv(const void *Q, const void *Kw, const void *Vw, const void *dO,
                        const float *LSE, const float *delta, const void *tasks,
                        const LayoutArgs &L, int grid, float scale, float *dk_pool, float *dv_pool,
-                       void *dS, const int32_t *q2k, hipStream_t s);
+                       void *dS, hipStream_t s);
 hipError_t backward_dqs(const void *dS, const void *Kt, const int32_t *q2k, const LayoutArgs &L,
                         const void *plan, float scale, void *dQ, hipStream_t s);
 hipError_t backward_dq(const void *Q, const void *dO, const void *Kw, const void *Vw, const void *Kt,

@@ -205,12 +205,14 @@ int msa_backward_preprocess(const msa_bf16 *O, const msa_bf16 *dO, int32_t num_t
  *     floor(c * rows_i / grid);
  *   meta at word msa_tasks_meta_offset(): Rmax x {r, n_valid, flags, k} (flags bit0 =
  *     first row of its bucket, bit1 = last);
- *   qrows then qpos: Rmax x 8 int32 each (query ids; document-local positions; -1 pad).
+ *   qrows, qpos, qtile: Rmax x 8 int32 each (query ids; document-local positions;
+ *     stored-dS tile index (t * 4 + i) * 16 + j with j the first slot of q2k[i][t]
+ *     listing the bucket's block; -1 pad).  q2k is the device q2k the CSR was built from.
  * Rows inside one bucket appear in ascending k; their query sets follow the CSR order.
  * --------------------------------------------------------------------------------- */
 size_t msa_tasks_meta_offset(int32_t grid);
 int msa_build_tasks(const msa_layout *layout, const int32_t *row_ptr, const int32_t *cols,
-                    int32_t grid, void *tasks, size_t tasks_bytes, void *stream);
+                    const int32_t *q2k, int32_t grid, void *tasks, size_t tasks_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * Backward (msa_backward_sm100 API page, run_backward and module summary):

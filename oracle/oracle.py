@@ -215,20 +215,24 @@ def forward_plan(q2k, cu_seqlens, nq: int, blk: int = 128):
 # Backward task tables + CTA walk ([BWD] summary: task rows of 8 queries x 16 heads,
 # bucketed by (index head, key block); [PR] Changelog: exact counts, CTA scheduling).
 # --------------------------------------------------------------------------------------
-def tasks(row_ptr, cols, cu_seqlens, num_index_heads: int, grid: int, blk: int = 128):
+def tasks(row_ptr, cols, cu_seqlens, num_index_heads: int, grid: int, blk: int = 128, q2k=None):
     """Task rows in ascending bucket order r; bucket r holds ceil(count_r / 8) rows and
     row k of it carries cols[row_ptr[r] + 8k : +8] (-1 padded).  Returns a dict:
     meta int32 [R, 4] = (r, n_valid, flags, k) with flags bit0 = first row of its
     bucket, bit1 = last; qrows int32 [R, 8]; qpos int32 [R, 8] (document-local
     positions, -1 padded); R; per-head row counts; cta [HI, grid+1] row bounds: in
     index head i, workgroup c walks rows [cta[i, c], cta[i, c+1]), with
-    cta[i, c] = off_i + floor(c * R_i / grid)."""
+    cta[i, c] = off_i + floor(c * R_i / grid).  With q2k given, also qslot int32 [R, 8]:
+    the first of the 16 q2k slots of (index head, query) that lists the bucket's
+    document-local block (-1 padded)."""
     row_ptr = np.asarray(row_ptr, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
     _, pos, _ = coords(cu_seqlens, blk)
     nrows = len(row_ptr) - 1
     NB = nrows // num_index_heads
-    meta, qrows, qpos = [], [], []
+    meta, qrows, qpos, qslot = [], [], [], []
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    ws = np.concatenate([[0], np.cumsum((np.diff(cu) + blk - 1) // blk * blk)])
     for r in range(nrows):
         c0, c1 = int(row_ptr[r]), int(row_ptr[r + 1])
         ntile = (c1 - c0 + TILE_QUERIES - 1) // TILE_QUERIES
@@ -239,6 +243,15 @@ def tasks(row_ptr, cols, cu_seqlens, num_index_heads: int, grid: int, blk: int =
             pad = TILE_QUERIES - len(ids)
             qrows.append(list(ids) + [-1] * pad)
             qpos.append([int(pos[t]) for t in ids] + [-1] * pad)
+            if q2k is not None:
+                i, gb = r // NB, r % NB
+                d = int(np.searchsorted(ws, gb * blk, side="right") - 1)  # document of block gb
+                bl = gb - int(ws[d]) // blk
+                sl = []
+                for t in ids:
+                    sel = [int(x) for x in q2k[i, t]]
+                    sl.append(sel.index(bl))
+                qslot.append(sl + [-1] * pad)
     R = len(meta)
     meta = np.array(meta, dtype=np.int32).reshape(R, 4)
     qrows = np.array(qrows, dtype=np.int32).reshape(R, TILE_QUERIES)
@@ -250,7 +263,10 @@ def tasks(row_ptr, cols, cu_seqlens, num_index_heads: int, grid: int, blk: int =
     for i in range(num_index_heads):
         for c in range(grid + 1):
             cta[i, c] = off[i] + (c * head_rows[i]) // grid
-    return dict(meta=meta, qrows=qrows, qpos=qpos, R=R, head_rows=head_rows, cta=cta)
+    out = dict(meta=meta, qrows=qrows, qpos=qpos, R=R, head_rows=head_rows, cta=cta)
+    if q2k is not None:
+        out["qslot"] = np.array(qslot, dtype=np.int32).reshape(R, TILE_QUERIES)
+    return out
 
 
 # --------------------------------------------------------------------------------------

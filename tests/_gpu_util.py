@@ -91,13 +91,17 @@ def check_structures(m, cu, q2k):
         np.testing.assert_array_equal(a, b)
     tk = m.task_tables()
     # the oracle's task builder on the GPU's own CSR order must reproduce the tables
-    otk = OR.tasks(rp, cols, cu, 4, m.grid)
+    otk = OR.tasks(rp, cols, cu, 4, m.grid, q2k=q2k)
     assert tk["R"] == otk["R"]
     np.testing.assert_array_equal(tk["head_rows"], otk["head_rows"])
     np.testing.assert_array_equal(tk["cta"], otk["cta"])
     np.testing.assert_array_equal(tk["meta"], otk["meta"])
     np.testing.assert_array_equal(tk["qrows"], otk["qrows"])
     np.testing.assert_array_equal(tk["qpos"], otk["qpos"])
+    # stored-dS tile index = (t * 4 + i) * 16 + the oracle's member slot
+    head = otk["meta"][:, 0:1] // ((len(orp) - 1) // 4)  # bucket r = i * NB + block
+    np.testing.assert_array_equal(tk["qtile"], np.where(otk["qrows"] >= 0,
+                                                        (otk["qrows"] * 4 + head) * 16 + otk["qslot"], -1))
     # and the canonical tables (sorted CSR) have the same per-bucket content
     ctk = OR.tasks(orp, ocols, cu, 4, m.grid)
     assert ctk["R"] == tk["R"]

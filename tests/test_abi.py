@@ -88,7 +88,7 @@ def test_argument_errors_return_before_device_use(M):
     assert lib.msa_plan(L.ref(), a, a, 16, None) == E["SCRATCH"]
     assert lib.msa_forward(a, a, a, a, L.ref(), a, ctypes.c_float(-1.0), a, a, None) == E["SHAPE"]
     assert lib.msa_backward_preprocess(a, a, 0, a, None) == E["SHAPE"]
-    assert lib.msa_build_tasks(L.ref(), a, a, 0, a, 1 << 30, None) == E["GRID"]
+    assert lib.msa_build_tasks(L.ref(), a, a, a, 0, a, 1 << 30, None) == E["GRID"]
     bw = lambda grid, mode, nbytes: lib.msa_backward(a, a, a, a, a, a, a, a, a, a, grid, L.ref(),
                                                      ctypes.c_float(0.1), mode, a, a, a, a, nbytes, None)
     assert bw(256, 9, 1 << 40) == E["MODE"]

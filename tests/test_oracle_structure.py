@@ -88,6 +88,38 @@ def _brute_tasks(rows, grid, HI):
     return np.array(meta).reshape(-1, 4), np.array(qrows).reshape(-1, 8)
 
 
+def test_task_member_slots_brute_force():
+    """Each task entry's member slot is the first of its query's q2k slots listing the
+    bucket's block (duplicates and unused slots planted)."""
+    cu, q2k = WL.make_custom([300, 41, 77, 129], "uniform", 9, num_index_heads=3, topk=7, blk=16)
+    q2k = WL.scatter_unused(q2k, 9)
+    q2k[1, 7, :2] = q2k[1, 7, 2]
+    q2k[2, 200, 3] = q2k[2, 200, 5]
+    row_ptr, cols = OR.k2q_csr(q2k, cu, 16)
+    tk = OR.tasks(row_ptr, cols, cu, 3, 5, blk=16, q2k=q2k)
+    cu_ws, W, NB = OR.layout(cu, 16)
+    # brute force: first slot of every (index head, query, document-local block)
+    first = {}
+    for i in range(3):
+        for t in range(int(cu[-1])):
+            for j in range(q2k.shape[2]):
+                first.setdefault((i, t, int(q2k[i, t, j])), j)
+    n = 0
+    for row in range(tk["R"]):
+        r, nv = int(tk["meta"][row, 0]), int(tk["meta"][row, 1])
+        i, gb = r // NB, r % NB
+        for s_ in range(8):
+            t = int(tk["qrows"][row, s_])
+            if s_ >= nv:
+                assert t == -1 and tk["qslot"][row, s_] == -1
+                continue
+            d = max(k for k in range(len(cu) - 1) if cu[k] <= t)
+            bl = gb - int(cu_ws[d]) // 16
+            assert tk["qslot"][row, s_] == first[(i, t, bl)]
+            n += 1
+    assert n == len(cols)
+
+
 @pytest.mark.parametrize("grid", [1, 3, 7, 64])
 def test_tasks_match_brute_force_and_cover_rows(grid):
     cu, q2k = WL.make_custom([300, 41, 77, 129], "uniform", 8, num_index_heads=3, topk=7, blk=16)
