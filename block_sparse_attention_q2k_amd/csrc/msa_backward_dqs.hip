@@ -10,10 +10,11 @@
 //
 // Design (gfx950): one workgroup of 4 waves per plan item (index head, up to
 // MSA_FWD_GROUP queries of one document), walking the item's list of member blocks like
-// the forward.  Per block the tiles of the active queries are copied into LDS slots by
-// the asynchronous global-to-LDS path (one 1 KB quarter per wave and tile) while the
-// previous block is computed, and so are the block's K^T slices into registers; one
-// wait and barrier per block.  Wave w owns head dims [32w, 32w + 32): dQ^T += K^T dS^T
+// the forward; two workgroups per CU, so that one computes while the other waits.  Per
+// step the tiles of the active queries (at most 8: a block with more active queries
+// takes two steps) are copied into LDS slots by the asynchronous global-to-LDS path
+// (one 1 KB quarter per wave and tile) while the previous step is computed, and so are
+// the block's K^T slices into registers; one wait and barrier per step.  Wave w owns head dims [32w, 32w + 32): dQ^T += K^T dS^T
 // with 16x16x32 MFMAs, K^T slices from the transposed-fragment workspace copy, the dS^T
 // fragments (keys of one head) read from the [key][head] tiles with the transposing
 // LDS read ds_read_b64_tr_b16.  dQ stays in accumulation registers for the whole walk
@@ -23,6 +24,7 @@
 namespace msa {
 
 constexpr int kDqsThreads = kWalkThreads;
+constexpr int kDqsSlots = 8;                 // tiles per LDS buffer: at most 8 queries per step
 constexpr int kDsTileBytes = kBlk * 16 * 2;  // 16 heads x 128 keys bf16
 constexpr int kCachePolicyNT = 2;            // cache-policy operand: nt (streaming)
 
@@ -89,6 +91,37 @@ __device__ __forceinline__ void dqs_accumulate(const bf16x8 (&kt)[2][4], const c
   }
 }
 
+// Walk steps: list entry a (block, query mask) is one step, or two when more than
+// kDqsSlots of its queries are active (the first kDqsSlots of them, then the rest).
+struct DqsStep {
+  int b;
+  uint32_t m;
+};
+__device__ __forceinline__ uint32_t first_units(uint32_t m, int k) {
+  uint32_t lo = 0;
+  for (int i = 0; i < k && m; ++i) {
+    const uint32_t bit = m & (0u - m);
+    lo |= bit;
+    m ^= bit;
+  }
+  return lo;
+}
+__device__ __forceinline__ DqsStep dqs_step(const int32_t *list, int a, int part) {
+  const int b = uniform(list[2 * a]);
+  const uint32_t m0 = (uint32_t)uniform(list[2 * a + 1]);
+  if (__popc(m0) <= kDqsSlots) return DqsStep{b, m0};
+  const uint32_t lo = first_units(m0, kDqsSlots);
+  return DqsStep{b, part ? m0 ^ lo : lo};
+}
+__device__ __forceinline__ void dqs_advance(const int32_t *list, int &a, int &part) {
+  if (part == 0 && __popc((uint32_t)uniform(list[2 * a + 1])) > kDqsSlots) {
+    part = 1;
+  } else {
+    ++a;
+    part = 0;
+  }
+}
+
 // Waits for every outstanding global access of this wave (loads and asynchronous LDS
 // copies), then for the whole workgroup.
 __device__ __forceinline__ void dqs_sync() {
@@ -98,12 +131,12 @@ __device__ __forceinline__ void dqs_sync() {
   asm volatile("" ::: "memory");
 }
 
-__global__ void __launch_bounds__(kDqsThreads, 1)
+__global__ void __launch_bounds__(kDqsThreads, 2)
 dqs_kernel(const uint16_t *__restrict__ dS, const uint16_t *__restrict__ Kt, const int32_t *__restrict__ q2k,
            int T, const int32_t *__restrict__ cu, const int32_t *__restrict__ cu_ws, int NB,
            const int32_t *__restrict__ plan, const int32_t *__restrict__ plan_len,
            const int32_t *__restrict__ plan_lists, float scale, uint16_t *__restrict__ dQ) {
-  __shared__ __attribute__((aligned(16))) char sT[2][kFwdGroup * kDsTileBytes];
+  __shared__ __attribute__((aligned(16))) char sT[2][kDqsSlots * kDsTileBytes];
   __shared__ int32_t sQ2K[kFwdGroup * kTopk];
   const int p = blockIdx.x;
   if (p >= plan[0]) return;
@@ -128,35 +161,44 @@ dqs_kernel(const uint16_t *__restrict__ dS, const uint16_t *__restrict__ Kt, con
   const size_t gblk0 = (size_t)i * NB + (size_t)(wsrow0 / kBlk);
   if (nact > 0) {
     bf16x8 kt0[2][4], kt1[2][4];
-    int b = uniform(list[0]);
-    uint32_t m = (uint32_t)uniform(list[1]);
+    int a = 0, part = 0;
+    DqsStep cur = dqs_step(list, 0, 0);
 #pragma unroll
-    for (int md = 0; md < 2; ++md) load_tslice(kt0[md], Kt, gblk0 + b, 32 * w.wave + 16 * md, w);
-    dqs_fetch_tiles(dS, sQ2K, sT[0], m, b, t0, i, w);
-    for (int a = 0; a < nact; a += 2) {
-      // ---- block a: its tiles and K^T slices arrived; fetch block a + 1's
+    for (int md = 0; md < 2; ++md) load_tslice(kt0[md], Kt, gblk0 + cur.b, 32 * w.wave + 16 * md, w);
+    dqs_fetch_tiles(dS, sQ2K, sT[0], cur.m, cur.b, t0, i, w);
+    while (true) {
+      // ---- step in buffer 0: its tiles and K^T slices arrived; fetch the next step's
       dqs_sync();
-      int bn = b;
-      uint32_t mn = 0;
-      if (a + 1 < nact) {
-        bn = uniform(list[2 * (a + 1)]);
-        mn = (uint32_t)uniform(list[2 * (a + 1) + 1]);
+      int an = a, pn = part;
+      dqs_advance(list, an, pn);
+      bool more = an < nact;
+      DqsStep nx = cur;
+      if (more) {
+        nx = dqs_step(list, an, pn);
 #pragma unroll
-        for (int md = 0; md < 2; ++md) load_tslice(kt1[md], Kt, gblk0 + bn, 32 * w.wave + 16 * md, w);
-        dqs_fetch_tiles(dS, sQ2K, sT[1], mn, bn, t0, i, w);
+        for (int md = 0; md < 2; ++md) load_tslice(kt1[md], Kt, gblk0 + nx.b, 32 * w.wave + 16 * md, w);
+        dqs_fetch_tiles(dS, sQ2K, sT[1], nx.m, nx.b, t0, i, w);
       }
-      dqs_accumulate(kt0, sT[0], m, __popc(m), w, acc);
-      if (a + 1 >= nact) break;
-      // ---- block a + 1
+      dqs_accumulate(kt0, sT[0], cur.m, __popc(cur.m), w, acc);
+      if (!more) break;
+      a = an;
+      part = pn;
+      cur = nx;
+      // ---- step in buffer 1
       dqs_sync();
-      if (a + 2 < nact) {
-        b = uniform(list[2 * (a + 2)]);
-        m = (uint32_t)uniform(list[2 * (a + 2) + 1]);
+      dqs_advance(list, an, pn);
+      more = an < nact;
+      if (more) {
+        nx = dqs_step(list, an, pn);
 #pragma unroll
-        for (int md = 0; md < 2; ++md) load_tslice(kt0[md], Kt, gblk0 + b, 32 * w.wave + 16 * md, w);
-        dqs_fetch_tiles(dS, sQ2K, sT[0], m, b, t0, i, w);
+        for (int md = 0; md < 2; ++md) load_tslice(kt0[md], Kt, gblk0 + nx.b, 32 * w.wave + 16 * md, w);
+        dqs_fetch_tiles(dS, sQ2K, sT[0], nx.m, nx.b, t0, i, w);
       }
-      dqs_accumulate(kt1, sT[1], mn, __popc(mn), w, acc);
+      dqs_accumulate(kt1, sT[1], cur.m, __popc(cur.m), w, acc);
+      if (!more) break;
+      a = an;
+      part = pn;
+      cur = nx;
     }
   }
   // ---- epilogue: acc[u][md][r] = dQ^T[dim 32w + 16md + 4g + r][head at tile position
