@@ -45,7 +45,7 @@ __device__ inline void kv_atomic_add(float *p, float v) {
   __builtin_amdgcn_global_atomic_fadd_f32((__attribute__((address_space(1))) float *)p, v);
 }
 
-// The 8 query ids and positions of a task row (uniform: scalar loads).
+// The 8 query ids and positions of a task row (uniform).
 struct KvRowIds {
   int t[kTileQ], pos[kTileQ];
 };
@@ -55,6 +55,23 @@ __device__ __forceinline__ void kv_row_ids(KvRowIds &ids, const int32_t *__restr
   for (int k = 0; k < kTileQ; ++k) {
     ids.t[k] = qrows[(size_t)row * kTileQ + (k < nv ? k : 0)];  // padding rows reuse a valid row
     ids.pos[k] = k < nv ? qpos[(size_t)row * kTileQ + k] : -1;    // ... and are masked
+  }
+}
+// A task row's ids as one register: lanes 0-7 its query ids, 8-15 their positions, 16-19
+// its meta entry {bucket, n_valid, flags, k}.  Loaded a row ahead with one vector load
+// (the row's scalar loads would otherwise miss the caches and stall the row's start).
+__device__ __forceinline__ int kv_ids_load(const int32_t *__restrict__ qrows, const int32_t *__restrict__ qpos,
+                                           const i32x4 *__restrict__ meta, int row, int lane) {
+  const int32_t *src = lane < 8    ? qrows + (size_t)row * kTileQ + lane
+                       : lane < 16 ? qpos + (size_t)row * kTileQ + (lane - 8)
+                                   : (const int32_t *)(meta + row) + ((lane - 16) & 3);
+  return lane < 20 ? *src : 0;
+}
+__device__ __forceinline__ void kv_ids_unpack(KvRowIds &ids, int v, int nv) {
+#pragma unroll
+  for (int k = 0; k < kTileQ; ++k) {
+    ids.t[k] = __builtin_amdgcn_readlane(v, k < nv ? k : 0);
+    ids.pos[k] = k < nv ? __builtin_amdgcn_readlane(v, 8 + k) : -1;
   }
 }
 
@@ -111,6 +128,7 @@ struct KvState {
   int cur_r, kbase, gb;
   float lse2, del;
   int pos, qt;  // qt: stored-dS tile index of the next row's query tid (tid < 8)
+  int idv;      // ids of the next row (kv_ids_load)
 };
 
 // One task row: compute from tile `cur` (+ its scalars), prefetch row + 1 into `nxt`.
@@ -154,9 +172,11 @@ __device__ __forceinline__ void kv_row(
   //    after the barrier, the gathers of all waves would queue up and stall the waves'
   //    instruction streams until accepted.
   const bool more = row + 1 < hi;
+  const int r_next = __builtin_amdgcn_readlane(st.idv, 16);
+  const int idv2 = row + 2 < hi ? kv_ids_load(qrows, qpos, meta, row + 2, lane) : 0;
   KvRowIds ids;
   if (more) {
-    kv_row_ids(ids, qrows, qpos, row + 1, meta[row + 1][1]);
+    kv_ids_unpack(ids, st.idv, __builtin_amdgcn_readlane(st.idv, 17));
     if (tid < 128) kv_scalars(LSE, Delta, ids, i, tid, st.lse2, st.del, st.pos);
     if (STORE_DS && tid < kTileQ) st.qt = qtile[(size_t)(row + 1) * kTileQ + tid];
   }
@@ -239,7 +259,7 @@ __device__ __forceinline__ void kv_row(
     }
   }
   // 4. end of this bucket's segment in this workgroup: flush dK/dV
-  if (!more || meta[row + 1][0] != r) {
+  if (!more || r_next != r) {
     // register e of dvacc[nd]: key 32w + 8(e/4) + 4h + e%4, dim 32nd + l32
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -257,6 +277,7 @@ __device__ __forceinline__ void kv_row(
   if (more && tid < 128) kv_store_scalars(nxt_sc, tid, st.lse2, st.del, st.pos);
   if (STORE_DS && more && tid < kTileQ) ((int32_t *)nxt_sc)[kKvScTile + tid] = st.qt;
   wait_vm();
+  st.idv = idv2;
   __syncthreads();
 }
 
@@ -284,6 +305,7 @@ bwd_kv_kernel(uint16_t *__restrict__ dS, const int32_t *__restrict__ qtile,
     {  // prologue: row lo into tile 0
       KvRowIds ids;
       kv_row_ids(ids, qrows, qpos, lo, meta[lo][1]);
+      st.idv = lo + 1 < hi ? kv_ids_load(qrows, qpos, meta, lo + 1, tid & 63) : 0;
       if (tid < 128) {
         kv_scalars(LSE, Delta, ids, i, tid, st.lse2, st.del, st.pos);
         kv_store_scalars(sc0, tid, st.lse2, st.del, st.pos);
