@@ -49,7 +49,7 @@ struct FwdCtx {
   float c;  // scale * log2(e)
   const char *sQ;
   char *sP;
-  float *sM, *sLw;  // references [unit][head]; row sums [wave][lane half][unit][head]
+  float *sM, *sX;  // references [unit][head]; exchange area [wave][unit][head]
 };
 
 // Workspace block index (KV head, block) of the item's block b.
@@ -105,16 +105,11 @@ __device__ __forceinline__ float fwd_tile_max(const f32x16 &st) {
   return fmaxf(mx, __shfl_xor(mx, 32));
 }
 
-// P = 2^(c s - mn) of the tile, as bf16, to the slots of its units (round slot s0 +
-// column half), and the row sums of those bf16 values (the numerators the PV phase
-// uses) over the lane's 16 keys into sLw[wave][hi][unit][head]; each entry has one
-// writer lane, so the adds keep program order.  `two`: the second half holds a unit
-// (otherwise its P lands in an unused slot and its sums are dropped); mn: this lane's
-// column reference.
-__device__ __forceinline__ void fwd_tile_p(const FwdCtx &x, const f32x16 &st, int u0, int u1, int s0,
-                                           bool two, float mn) {
+// P = 2^(c s - mn) of the tile, as bf16, to the slots of its units (slot s0 + column
+// half).  `two`: the second half holds a unit (otherwise its P lands in an unused
+// slot); mn: this lane's column reference.  The row sums are taken in the PV phase.
+__device__ __forceinline__ void fwd_tile_p(const FwdCtx &x, const f32x16 &st, int s0, float mn) {
   const int half = x.w.l32 >> 4;
-  const int u = half ? u1 : u0;
   uint32_t pk[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
@@ -123,13 +118,6 @@ __device__ __forceinline__ void fwd_tile_p(const FwdCtx &x, const f32x16 &st, in
   char *prow = x.sP + (s0 + half) * kSlotStride + slot_store_offset(x.w);
 #pragma unroll
   for (int j = 0; j < 4; ++j) *(u32x2 *)(prow + 16 * j) = u32x2{pk[2 * j], pk[2 * j + 1]};
-  float sa = 0.f, sb = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; j += 2) {
-    sa = sum_bf16x2(pk[j], sa);
-    sb = sum_bf16x2(pk[j + 1], sb);
-  }
-  if (!half || two) atomicAdd(x.sLw + ((x.w.wave * 2 + x.w.hi) * kFwdGroup + u) * 16 + x.w.l16, sa + sb);
 }
 
 // LDS operands of one pair of the S phase, read ahead of its MFMAs.
@@ -160,14 +148,13 @@ __device__ __forceinline__ void fwd_scores(const FwdCtx &x, const bf16x8 (&k)[8]
   fwd_pair_load(x, pr, ms);
   for (int s0 = 0;; s0 += 2) {
     const int u0 = pr.u0, u1 = pr.u1;
-    const bool two = pr.two;
     const float mn = pr.mn;
     const bool diag = fwd_tile_diag(dmask, u0, u1);
     f32x16 st = tile32(k, pr.q);
     const bool more = ms != 0;
     if (more) fwd_pair_load(x, pr, ms);
     fwd_tile_mask(x, st, u0, u1, b, diag);
-    fwd_tile_p(x, st, u0, u1, s0, two, mn);
+    fwd_tile_p(x, st, s0, mn);
     if (!more) break;
   }
 }
@@ -180,11 +167,25 @@ __device__ __forceinline__ void fwd_pv_mfma(const bf16x8 (&v)[2][4], const bf16x
     for (int md = 0; md < 2; ++md) acc[md] = mfma16(v[md][kk], pf[kk], acc[md]);
 }
 
+// Sum of the 32 bf16 P values of a unit's P^T fragments (keys 32 kk + 8 g + 0..7 of the
+// lane's head), in fp32: the lane's share of the row sum over this block's keys.
+__device__ __forceinline__ float fwd_frag_sum(const bf16x8 (&pf)[4]) {
+  float s[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const u32x4 p = __builtin_bit_cast(u32x4, pf[kk]);
+    s[kk] = sum_bf16x2(p[3], sum_bf16x2(p[2], sum_bf16x2(p[1], sum_bf16x2(p[0], 0.f))));
+  }
+  return (s[0] + s[1]) + (s[2] + s[3]);
+}
+
 // PV phase of one step: O^T[dims 32w.., heads] += V^T P^T for the nr units of mr,
-// whose P slots are their ranks in mr.  After a unit's MFMAs are issued, the same
-// registers are refilled with the next slot's fragments.
+// whose P slots are their ranks in mr, and row sums of the same bf16 P values the
+// products use: the step's k-th unit is summed by wave k % 4, into ls[u] (this lane's
+// keys).  After a unit's MFMAs are issued,
+// the same registers are refilled with the next slot's fragments.
 __device__ __forceinline__ void fwd_pv(const FwdCtx &x, const bf16x8 (&v)[2][4], uint32_t mr, int nr,
-                                       f32x4 (&acc)[kFwdGroup][2]) {
+                                       f32x4 (&acc)[kFwdGroup][2], float (&ls)[kFwdGroup]) {
   bf16x8 pf[4];
   load_slot(pf, x.sP, 0, x.w);
   int k = 0;
@@ -192,6 +193,7 @@ __device__ __forceinline__ void fwd_pv(const FwdCtx &x, const bf16x8 (&v)[2][4],
   for (int u = 0; u < kFwdGroup; ++u) {
     if ((mr >> u) & 1u) {
       fwd_pv_mfma(v, pf, acc[u]);
+      if ((k & 3) == x.w.wave) ls[u] += fwd_frag_sum(pf);  // the step's k-th unit: wave k % 4
       k = uniform(k + 1);
       load_slot(pf, x.sP, min(k, nr - 1), x.w);
     }
@@ -221,10 +223,10 @@ __device__ __forceinline__ void fwd_references(const FwdCtx &x, const bf16x8 (&k
 }
 
 // Exact-reference pass: folds the maximum of block b over all keys into sM for every
-// unit in `units`.  The per-wave maxima go through sX (the row-sum area, unused in
-// this pass); every wave then stores the same folded value.
+// unit in `units`.  The per-wave maxima go through sX; every wave then stores the same
+// folded value.
 __device__ __forceinline__ void fwd_fold_max(const FwdCtx &x, const bf16x8 (&k)[8], uint32_t units, int b) {
-  float *sX = x.sLw;
+  float *sX = x.sX;
   for (uint32_t us = units; us;) {
     const int u0 = pop_unit(us);
     const bool two = us != 0;
@@ -285,7 +287,7 @@ __device__ __forceinline__ void fwd_pos_advance(FwdPos &q) {
 template <bool MAXPASS>
 __device__ __forceinline__ void fwd_step(const FwdCtx &x, int a, FwdPos &q, const bf16x8 (&kc)[8],
                                          const bf16x8 (&vc)[2][4], bf16x8 (&kn)[8], bf16x8 (&vn)[2][4],
-                                         f32x4 (&acc)[kFwdGroup][2], uint32_t &seen) {
+                                         f32x4 (&acc)[kFwdGroup][2], float (&ls)[kFwdGroup], uint32_t &seen) {
   const int b = q.b;
   const uint32_t m = q.m;
   const int nu = __popc(m);
@@ -316,7 +318,7 @@ __device__ __forceinline__ void fwd_step(const FwdCtx &x, int a, FwdPos &q, cons
   fwd_load_v_half<0>(x, vn, q.bn);
   WAIT_VMCNT(12);  // this step's V^T slices
   // ---- PV phase
-  fwd_pv(x, vc, m, nu, acc);
+  fwd_pv(x, vc, m, nu, acc, ls);
   fwd_load_v_half<1>(x, vn, q.bn);
   lds_barrier();  // P slots are rewritten by the next step
   fwd_pos_advance(q);
@@ -325,7 +327,8 @@ __device__ __forceinline__ void fwd_step(const FwdCtx &x, int a, FwdPos &q, cons
 // The whole walk over the item's list.  seen0 = ~0 keeps the references already in
 // sM (the exact maxima of the max pass).
 template <bool MAXPASS>
-__device__ __forceinline__ void fwd_walk(const FwdCtx &x, f32x4 (&acc)[kFwdGroup][2], uint32_t seen0) {
+__device__ __forceinline__ void fwd_walk(const FwdCtx &x, f32x4 (&acc)[kFwdGroup][2], float (&ls)[kFwdGroup],
+                                         uint32_t seen0) {
   if (x.nact <= 0) return;
   bf16x8 k0[8], k1[8], v0[2][4], v1[2][4];
   uint32_t seen = seen0;
@@ -334,8 +337,8 @@ __device__ __forceinline__ void fwd_walk(const FwdCtx &x, f32x4 (&acc)[kFwdGroup
   fwd_load_k(x, k0, q.b);
   if (!MAXPASS) fwd_load_v(x, v0, q.b);
   for (int a = 0; a < x.nact; a += 2) {
-    fwd_step<MAXPASS>(x, a, q, k0, v0, k1, v1, acc, seen);
-    if (a + 1 < x.nact) fwd_step<MAXPASS>(x, a + 1, q, k1, v1, k0, v0, acc, seen);
+    fwd_step<MAXPASS>(x, a, q, k0, v0, k1, v1, acc, ls, seen);
+    if (a + 1 < x.nact) fwd_step<MAXPASS>(x, a + 1, q, k1, v1, k0, v0, acc, ls, seen);
   }
 }
 
@@ -350,7 +353,7 @@ fwd_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
            float scale_log2e, uint16_t *__restrict__ O, float *__restrict__ LSE) {
   __shared__ __attribute__((aligned(16))) char sQ[kFwdGroup * 16 * kUnitRow];
   __shared__ __attribute__((aligned(16))) char sP[kFwdSlots * kSlotStride];
-  __shared__ float sM[kFwdGroup * 16], sLw[kWalkWaves * 2 * kFwdGroup * 16];
+  __shared__ float sM[kFwdGroup * 16], sX[kWalkWaves * kFwdGroup * 16];
   __shared__ int sBad;
   const int p = blockIdx.x;
   if (p >= plan[0]) return;
@@ -366,7 +369,7 @@ fwd_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
   x.nact = uniform(plan_len[p]);
   x.list = plan_lists + (size_t)2 * kPlanMaxList * p;
   x.c = scale_log2e;
-  x.sQ = sQ; x.sP = sP; x.sM = sM; x.sLw = sLw;
+  x.sQ = sQ; x.sP = sP; x.sM = sM; x.sX = sX;
   const int tid = x.w.tid;
 
   // Q rows of the item (16 rows of 256 B per unit) into sQ
@@ -376,21 +379,33 @@ fwd_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
   if (tid == 0) sBad = 0;
   __syncthreads();
   f32x4 acc[kFwdGroup][2];
+  float ls[kFwdGroup];  // row sums: this lane's keys 8 g .. 8 g + 7 of every 32
 #pragma unroll
-  for (int u = 0; u < kFwdGroup; ++u) acc[u][0] = acc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (REDO) fwd_walk<true>(x, acc, 0u);  // sM = exact row maxima
-  for (int k = tid; k < kWalkWaves * 2 * kFwdGroup * 16; k += kWalkThreads) sLw[k] = 0.f;
-  __syncthreads();
-  fwd_walk<false>(x, acc, REDO ? ~0u : 0u);
-  __syncthreads();
-  // row sums in a fixed order; sLw[0][..] holds the total from here on
-  float *sL = sLw;
-  for (int k = tid; k < kFwdGroup * 16; k += kWalkThreads) {
-    float l = 0.f;
-#pragma unroll
-    for (int w = 0; w < 2 * kWalkWaves; ++w) l += sLw[w * kFwdGroup * 16 + k];
-    sL[k] = l;
+  for (int u = 0; u < kFwdGroup; ++u) {
+    acc[u][0] = acc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ls[u] = 0.f;
   }
+  if (REDO) {
+    fwd_walk<true>(x, acc, ls, 0u);  // sM = exact row maxima
+    __syncthreads();
+  }
+  fwd_walk<false>(x, acc, ls, REDO ? ~0u : 0u);
+  // row sums: the four 16-lane groups of every wave, then the four waves, add up in a
+  // fixed order into sL[unit][head]
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kFwdGroup; ++u) {
+    float l = ls[u] + __shfl_xor(ls[u], 16);
+    l += __shfl_xor(l, 32);
+    if (x.w.lane < 16) sX[(x.w.wave * kFwdGroup + u) * 16 + x.w.l16] = l;
+  }
+  __syncthreads();
+  float *sL = sX;  // sL[unit][head] = sum over the waves, written over wave 0's part
+  float lt = 0.f;
+  if (tid < kFwdGroup * 16)
+    lt = (sX[tid] + sX[kFwdGroup * 16 + tid]) + (sX[2 * kFwdGroup * 16 + tid] + sX[3 * kFwdGroup * 16 + tid]);
+  __syncthreads();
+  if (tid < kFwdGroup * 16) sL[tid] = lt;
   __syncthreads();
   // ---- epilogue: acc[u][md][r] = O^T[dim 32w + 16md + 4g + r][head l16]
 #pragma unroll
