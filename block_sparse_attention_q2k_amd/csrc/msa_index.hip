@@ -350,20 +350,23 @@ __global__ void plan_cost_kernel(const int32_t *__restrict__ q2k, const int32_t 
 }
 
 // One workgroup per index head: stable counting sort of its groups by cost,
-// descending; item p = rank * 4 + i.
+// descending; item p = rank * 4 + i.  rank = (groups of higher cost) + (earlier groups
+// of the same cost); the second term, per chunk of 1024 groups, from a match within
+// each wave (one ballot per distinct cost in the wave) and per-wave counts.
 __global__ void __launch_bounds__(1024)
 plan_sort_kernel(int Gmax, int32_t *__restrict__ plan, const i32x4 *__restrict__ ginfo,
                  const int32_t *__restrict__ cost) {
   constexpr int kMaxCost = kFwdGroup * kTopk;
+  constexpr int kWaves = 1024 / 64;
   __shared__ int32_t hist[kMaxCost + 1];
   __shared__ int32_t start[kMaxCost + 1];
-  __shared__ int32_t chunk[1024];
-  int i = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
-  int G = plan[1];
+  __shared__ int32_t wcount[kWaves][kMaxCost + 1];  // this chunk's count per wave and cost
+  const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = plan[1];
   const int32_t *c = cost + (size_t)i * Gmax;
-  for (int k = tid; k <= kMaxCost; k += nt) hist[k] = 0;
+  for (int k = tid; k <= kMaxCost; k += 1024) hist[k] = 0;
   __syncthreads();
-  for (int g = tid; g < G; g += nt) atomicAdd(&hist[c[g]], 1);
+  for (int g = tid; g < G; g += 1024) atomicAdd(&hist[c[g]], 1);
   __syncthreads();
   if (tid == 0) {  // start[v] = number of groups with cost > v
     int run = 0;
@@ -372,29 +375,37 @@ plan_sort_kernel(int Gmax, int32_t *__restrict__ plan, const i32x4 *__restrict__
       run += hist[v];
     }
   }
-  __syncthreads();
-  for (int base = 0; base < G; base += nt) {
-    int g = base + tid;
-    int my = g < G ? c[g] : -1;
-    chunk[tid] = my;
+  for (int base = 0; base < G; base += 1024) {
+    for (int k = tid; k < kWaves * (kMaxCost + 1); k += 1024) (&wcount[0][0])[k] = 0;
     __syncthreads();
-    if (g < G) {
-      int before = 0;
-      for (int j = 0; j < tid; ++j) before += (chunk[j] == my);
-      int rank = start[my] + before;
-      i32x4 gi = ginfo[g];
+    const int g = base + tid;
+    const int my = g < G ? c[g] : -1;
+    // lanes of this wave holding the same cost (invalid lanes form their own class)
+    uint64_t rest = ~0ull, peers = 0;
+    while (rest) {
+      const int lead = (int)__builtin_ctzll(rest);
+      const int v = __builtin_amdgcn_readlane(my, lead);
+      const uint64_t same = (uint64_t)__ballot(my == v);
+      if (my == v) peers = same;
+      rest &= ~same;
+    }
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const int in_wave = __popcll(peers & below);
+    if (my >= 0 && in_wave == 0) wcount[wave][my] = __popcll(peers);
+    __syncthreads();
+    if (my >= 0) {
+      int before = in_wave;
+      for (int w = 0; w < wave; ++w) before += wcount[w][my];
+      const int rank = start[my] + before;
+      const i32x4 gi = ginfo[g];
       ((i32x4 *)(plan + kPlanHeaderWords))[rank * kHI + i] = i32x4{i, gi[0], gi[1], gi[2]};
     }
     __syncthreads();
     // advance the per-cost starts by this chunk's counts
-    if (g < G) {
-      int last = 1;
-      for (int j = tid + 1; j < nt && base + j < G; ++j) last &= (chunk[j] != my);
-      if (last) {
-        int cnt = 0;
-        for (int j = 0; j <= tid; ++j) cnt += (chunk[j] == my);
-        start[my] += cnt;
-      }
+    for (int v = tid; v <= kMaxCost; v += 1024) {
+      int n = 0;
+      for (int w = 0; w < kWaves; ++w) n += wcount[w][v];
+      start[v] += n;
     }
     __syncthreads();
   }
@@ -447,9 +458,15 @@ __global__ void tasks_fill_kernel(const int32_t *__restrict__ row_ptr, const int
   qpos[(size_t)row * kTileQ + s] = t - cu[d];
   {
     const int i = r / NB, bl = gb - cu_ws[d] / kBlk;
-    const int32_t *sel = q2k + ((size_t)i * T + t) * kTopk;
-    int j = 0;
-    while (j < kTopk - 1 && sel[j] != bl) ++j;  // the CSR entry exists, so some slot lists bl
+    const i32x4 *sel = (const i32x4 *)(q2k + ((size_t)i * T + t) * kTopk);
+    int j = kTopk - 1;  // the CSR entry exists, so some slot lists bl: the first one wins
+#pragma unroll
+    for (int q = kTopk / 4 - 1; q >= 0; --q) {
+      const i32x4 v = sel[q];
+#pragma unroll
+      for (int e = 3; e >= 0; --e)
+        if (v[e] == bl) j = 4 * q + e;
+    }
     qtile[(size_t)row * kTileQ + s] = (t * kHI + i) * kTopk + j;
   }
   if (s == 0) {
