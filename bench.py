@@ -82,8 +82,8 @@ def cpu_baseline(cfg, budget_tokens):
 TRAFFIC_SOURCES = ["msa_backward_kv.hip", "msa_backward_dq.hip", "msa_backward_dqs.hip", "msa_walk.h", "msa_device.h",
                    "msa_launch.h"]
 TRAFFIC_RECORD = {"config": 2, "dq_mode": "stored",
-                  "sha256": "d3b516cb135ad42498210627c90c48b1496d73650c6d2a3d754bc33067b2f4ad",
-                  "bytes": 17157146537}  # read 12.645 GB + written 4.512 GB
+                  "sha256": "c5d11adeced55d8fa5bd20092157b66b88c2e95462b4645cdd0ba2658940d285",
+                  "bytes": 17025173572}  # read 12.513 GB + written 4.512 GB
 
 
 def sources_digest():
