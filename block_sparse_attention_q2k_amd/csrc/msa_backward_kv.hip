@@ -193,20 +193,30 @@ __device__ __forceinline__ void kv_row(
 #pragma unroll 1
   for (int half = 0; half < 2; ++half) {
     if (more) kv_gather_part<0>(Q, dO, ids, i, nxt, tid, half);
-    const i32x4 tix = STORE_DS ? *(const i32x4 *)((const int32_t *)cur_sc + kKvScTile + 4 * half) : i32x4{};
     f32x16 sacc[2], pacc[2];
 #pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2) {
-      const int mt = 2 * half + m2;
+    for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[m2][e] = pacc[m2][e] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const uint32_t off = swz_kv(32 * mt + l32, (16 * ks + 8 * h) * 2);
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2) {
+        const uint32_t off = swz_kv(32 * (2 * half + m2) + l32, (16 * ks + 8 * h) * 2);
         sacc[m2] = mfma32(*(const bf16x8 *)(cur + off), st.kf[ks], sacc[m2]);
         pacc[m2] = mfma32(*(const bf16x8 *)(cur + 32768 + off), st.vf[ks], pacc[m2]);
       }
     }
+    // order of the block above: the first 8 operand reads, then one MFMA and one read at a
+    // time, then the last 8 MFMAs (left to itself the scheduler issues each read right
+    // before its MFMA and waits for it)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads
+#pragma unroll
+    for (int z = 0; z < 24; ++z) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     if (more) kv_gather_part<2>(Q, dO, ids, i, nxt, tid, half);
     // P, dS: register e of sacc[m2] is row 32mt + 8(e/4) + 4h + e%4, query 2mt + e/8
     const uint32_t vh = vis >> (4 * half);
@@ -227,6 +237,7 @@ __device__ __forceinline__ void kv_row(
         }
       }
     }
+    const i32x4 tix = STORE_DS ? *(const i32x4 *)((const int32_t *)cur_sc + kKvScTile + 4 * half) : i32x4{};
     // dV += P^T dO, dK += dS^T Q: M = keys, N = dims (4 x 32), K = rows (16 per step)
 #pragma unroll
     for (int k2 = 0; k2 < 4; ++k2) {
