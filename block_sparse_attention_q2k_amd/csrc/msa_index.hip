@@ -22,55 +22,45 @@ __global__ void fill_u32_kernel(uint32_t *__restrict__ p, size_t n, uint32_t v) 
 }
 
 // ------------------------------------------------------------------ K/V alignment
-// Row-fragment workspace copies: one thread per 16-byte chunk (8 dims of one key of
-// one KV head) of a workspace row; rows past a document's end are zero.
-__global__ void align_kv_kernel(const u32x4 *__restrict__ K, const u32x4 *__restrict__ V,
-                                const int32_t *__restrict__ cu, const int32_t *__restrict__ cu_ws,
-                                int ndocs, int W, int NB, uint16_t *__restrict__ Kw, uint16_t *__restrict__ Vw) {
-  size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (size_t)W * 64) return;
-  const int w = (int)(gid >> 6), c = (int)(gid & 63);
-  const int d = upper_index(cu_ws, ndocs - 1, w);
-  const int p = w - cu_ws[d];
-  u32x4 k = {0, 0, 0, 0}, v = {0, 0, 0, 0};
-  if (p < cu[d + 1] - cu[d]) {
-    size_t src = (size_t)(cu[d] + p) * 64 + c;
-    k = K[src];
-    v = V[src];
-  }
-  const int kv = c >> 4, gb = w / kBlk, key = w % kBlk;
-  const size_t dst = ((size_t)kv * NB + gb) * kFragBlock + frag_row_off(key, (c & 15) * 8);
-  *(u32x4 *)(Kw + dst) = k;
-  *(u32x4 *)(Vw + dst) = v;
-}
-
-// Transposed-fragment copies of the workspace blocks, from the row fragments (the MFMA
-// A operands of V^T P^T and K^T dS^T).  One workgroup per (block, KV head, tensor).
+// Both workspace copies of one (block, KV head, tensor) per workgroup: the block's 128
+// rows (zero past the document's end) are read once, coalesced, into LDS and written out
+// as row fragments and as transposed fragments, each with contiguous 16-byte stores.
 __global__ void __launch_bounds__(256)
-transpose_blocks_kernel(const uint16_t *__restrict__ Kw, const uint16_t *__restrict__ Vw, int NB,
-                        uint16_t *__restrict__ Kt, uint16_t *__restrict__ Vt) {
+align_blocks_kernel(const u32x4 *__restrict__ K, const u32x4 *__restrict__ V, const int32_t *__restrict__ cu,
+                    const int32_t *__restrict__ cu_ws, int ndocs, int NB, uint16_t *__restrict__ Kw,
+                    uint16_t *__restrict__ Vw, uint16_t *__restrict__ Kt, uint16_t *__restrict__ Vt) {
   __shared__ uint32_t tile[128 * 65];  // 128 keys x 128 dims bf16, rows padded to 260 B
   const int gb = blockIdx.x, kv = blockIdx.y, tid = threadIdx.x;
-  const size_t fb = ((size_t)kv * NB + gb) * kFragBlock;
-  const uint16_t *X = (blockIdx.z ? Vw : Kw) + fb;
-  uint16_t *Y = (blockIdx.z ? Vt : Kt) + fb;
+  const u32x4 *X = blockIdx.z ? V : K;
+  const int d = upper_index(cu_ws, ndocs - 1, gb * kBlk);
+  const int p0 = gb * kBlk - cu_ws[d], len = cu[d + 1] - cu[d], t0 = cu[d];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int id = tid + 256 * k, key = id >> 4, c = id & 15;
-    const u32x4 v = *(const u32x4 *)(X + frag_row_off(key, c * 8));
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (p0 + key < len) v = X[((size_t)(t0 + p0 + key) * kHKV + kv) * 16 + c];
 #pragma unroll
     for (int q = 0; q < 4; ++q) tile[key * 65 + 4 * c + q] = v[q];
   }
   __syncthreads();
+  const size_t fb = ((size_t)kv * NB + gb) * kFragBlock;
+  uint16_t *Yw = (blockIdx.z ? Vw : Kw) + fb, *Yt = (blockIdx.z ? Vt : Kt) + fb;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {  // row fragments: chunk j holds key, dims dim .. dim + 7
+    const int j = tid + 256 * k;
+    const int key = ((j >> 9) << 5) | (j & 31), dim = (((j >> 6) & 7) << 4) | (((j >> 5) & 1) << 3);
+    const uint32_t *src = tile + key * 65 + (dim >> 1);
+    *(u32x4 *)(Yw + 8 * j) = u32x4{src[0], src[1], src[2], src[3]};
+  }
   const uint16_t *t16 = (const uint16_t *)tile;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < 8; ++k) {  // transposed fragments: 8 keys of one dim per chunk
     const int id = tid + 256 * k, dim = id >> 4, c = id & 15;
     uint32_t w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       w[q] = (uint32_t)t16[(8 * c + 2 * q) * 130 + dim] | ((uint32_t)t16[(8 * c + 2 * q + 1) * 130 + dim] << 16);
-    *(u32x4 *)(Y + frag_t_off(8 * c, dim)) = u32x4{w[0], w[1], w[2], w[3]};
+    *(u32x4 *)(Yt + frag_t_off(8 * c, dim)) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -558,11 +548,9 @@ hipError_t fill_u32(void *p, size_t n, uint32_t v, hipStream_t s) {
 
 hipError_t align_kv(const void *K, const void *V, const LayoutArgs &L, void *Kw, void *Vw,
                     void *Kt, void *Vt, hipStream_t s) {
-  size_t n = (size_t)L.W * 64;
-  hipLaunchKernelGGL(align_kv_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s, (const u32x4 *)K,
-                     (const u32x4 *)V, L.cu, L.cu_ws, L.ndocs, L.W, L.NB, (uint16_t *)Kw, (uint16_t *)Vw);
-  hipLaunchKernelGGL(transpose_blocks_kernel, dim3(L.NB, kHKV, 2), dim3(256), 0, s,
-                     (const uint16_t *)Kw, (const uint16_t *)Vw, L.NB, (uint16_t *)Kt, (uint16_t *)Vt);
+  hipLaunchKernelGGL(align_blocks_kernel, dim3(L.NB, kHKV, 2), dim3(256), 0, s, (const u32x4 *)K,
+                     (const u32x4 *)V, L.cu, L.cu_ws, L.ndocs, L.NB, (uint16_t *)Kw, (uint16_t *)Vw,
+                     (uint16_t *)Kt, (uint16_t *)Vt);
   return hipGetLastError();
 }
 
