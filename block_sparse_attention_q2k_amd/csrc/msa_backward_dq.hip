@@ -1,4 +1,5 @@
-// msa_backward_dq.hip -- query-parallel dQ of the MSA prefill backward for gfx950.
+// msa_backward_dq.hip -- query-parallel dQ of the MSA prefill backward by recomputation
+// (MSA_DQ_RECOMPUTE), gfx950.
 //
 // What is computed (msa_backward_sm100 API page, run_backward; the backward of the
 // operator in "feat(minimax-m3): add SM100 MSA sparse attention with custom

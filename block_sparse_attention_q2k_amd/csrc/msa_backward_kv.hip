@@ -5,8 +5,9 @@
 // the block's 128 keys: S = Q K^T, P = exp(scale S - LSE) under the causal mask,
 // dP = dO V^T, dS = P (dP - delta), dV += P^T dO, dK += scale dS^T Q.  dK/dV
 // accumulate in registers over the consecutive rows of one bucket and are flushed
-// with fp32 atomics at the end of the bucket segment.  dQ is produced by the
-// query-parallel kernel in msa_backward_dq.hip.
+// with fp32 atomics at the end of the bucket segment.  dQ is produced by a
+// query-parallel kernel: from the bf16 dS tiles this kernel stores (STORE_DS,
+// msa_backward_dqs.hip) or by recomputation (msa_backward_dq.hip).
 //
 // Design (gfx950): persistent grid; workgroup c walks, per index head, the task rows
 // [cta[i][c], cta[i][c+1]).  Four waves, wave w owns keys [32w, 32w+32): K and V

@@ -16,13 +16,14 @@
 //               P (bf16) and stores P to the units' LDS slots;
 //   PV phase -- wave w owns head dims [32w, 32w + 32) and updates O^T += V^T P^T for
 //               every active unit (16x16x32 MFMAs); its V^T rows come straight from
-//               the transposed workspace copy into registers, P^T from LDS.
+//               the transposed workspace copy into registers, P^T from LDS.  The row
+//               sums of the same bf16 P values are taken here too (one wave per unit).
 // With one wave per SIMD nothing hides an LDS read's latency but the wave's own
 // instruction stream, so the LDS operands of the next pair / unit are read before
 // the current one's MFMAs are issued.
 // The O accumulators of all units stay in accumulation registers for the whole walk;
-// the K registers of the next block are loaded one step ahead, the V^T registers at
-// the start of the step (they are first needed after the S phase).
+// the K rows and V^T slices of the next block are loaded during the current step, in
+// four groups spread over it.
 //
 // Softmax reference: each row's exponent reference m is the (base-2, scaled) maximum
 // of its first block and never moves, so the accumulators are never rescaled and the

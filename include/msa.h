@@ -118,7 +118,8 @@ size_t msa_csr_cols_capacity(const msa_layout *layout);
 size_t msa_plan_bytes(const msa_layout *layout);
 /* Bytes of the backward task buffer for a grid of `grid` workgroups. */
 size_t msa_tasks_bytes(const msa_layout *layout, int32_t grid);
-/* Bytes of the backward scratch (dQ pool of `dq_accum_mode`, if any; fp32 dK/dV pools). */
+/* Bytes of the backward scratch (dQ pool of `dq_accum_mode`, if any; fp32 dK/dV pools;
+ * MSA_DQ_STORED: the dS tiles, 256 KiB per token). */
 size_t msa_bwd_scratch_bytes(const msa_layout *layout, int dq_accum_mode);
 /* Grid size msa_build_tasks / msa_backward use by default (one workgroup per CU). */
 int32_t msa_default_grid(void);
@@ -222,7 +223,10 @@ int msa_build_tasks(const msa_layout *layout, const int32_t *row_ptr, const int3
  *   KV-parallel launch uses that many workgroups).  Writes dQ bf16 [T, 64, 128] and
  *   dK, dV bf16 [T, 4, 128] in compact token order.  scratch >=
  *   msa_bwd_scratch_bytes(layout, dq_accum_mode): the dQ pool of the pooled modes and
- *   fp32 dK/dV pools, zeroed by this call.
+ *   fp32 dK/dV pools, zeroed by this call, then (MSA_DQ_STORED) the dS tiles, 4 KiB per
+ *   (token, index head, q2k slot), written before they are read (not zeroed).  The
+ *   scratch holds no state between calls.  Calls that share a scratch buffer must not
+ *   overlap.
  * --------------------------------------------------------------------------------- */
 int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, const msa_bf16 *Kt,
                  const msa_bf16 *dO, const float *LSE, const float *delta, const int32_t *q2k,
