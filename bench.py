@@ -82,7 +82,7 @@ def cpu_baseline(cfg, budget_tokens):
 TRAFFIC_SOURCES = ["msa_backward_kv.hip", "msa_backward_dq.hip", "msa_backward_dqs.hip", "msa_walk.h", "msa_device.h",
                    "msa_launch.h"]
 TRAFFIC_RECORD = {"config": 2, "dq_mode": "stored",
-                  "sha256": "e373da84b752b4c73f32324e0e757bb22a6f40f1d11f5a969aae24ac87bcb57a",
+                  "sha256": "7f90c686c1d7dc1113839d13590dec7e62303ca9a832a739f4118c73d111c448",
                   "bytes": 17021817971}  # read 12.510 GB + written 4.512 GB
 
 
