@@ -68,6 +68,22 @@ def test_backward_parity_small(name, mode):
     check_close("dV", to_np(out["dV"]), dV)
 
 
+@pytest.mark.parametrize("grid", [1, 7, 1000])
+def test_backward_parity_grids(grid):
+    """The KV-parallel walk at other grid sizes: one workgroup per index head walking
+    every task row, buckets split between workgroups (their dK/dV parts added
+    atomically), and workgroups with empty or one-row ranges."""
+    say("case uniform_3docs_ragged grid", grid)
+    cu, q2k, tens = _small("uniform_3docs_ragged", scatter=True)
+    m, out = run_gpu(cu, q2k, tens, mode=3, grid=grid)
+    assert check_structures(m, cu, q2k) == 0
+    Q, K, V, dO = inputs64(tens)
+    dQ, dK, dV, _, _ = OR.backward(Q, K, V, dO, q2k, cu, SCALE)
+    check_close("dQ", to_np(out["dQ"]), dQ)
+    check_close("dK", to_np(out["dK"]), dK)
+    check_close("dV", to_np(out["dV"]), dV)
+
+
 def test_invalid_ids_flagged_and_ignored():
     """Out-of-range and repeated ids set the status bits and add no keys."""
     cu, q2k, tens = _small("uniform_3docs_ragged")
