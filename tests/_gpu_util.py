@@ -56,17 +56,17 @@ def check_lse(gpu, ref, mask=None):
     return check_close("LSE", g[~ninf], r[~ninf])
 
 
-def run_gpu(cu, q2k, tens, mode=3, grid=None, backward=True):
+def run_gpu(cu, q2k, tens, mode=3, grid=None, backward=True, scale=SCALE):
     """Forward (+ backward) of the HIP path on cuda:0.  Returns (msa object, outputs)."""
     M = msa_module()
     dev = "cuda:0"
     m = M.MSA(cu, grid=grid, dq_mode=mode, device=dev)
     Q, K, V, dO = (tens[k].to(dev) for k in ("Q", "K", "V", "dO"))
     q = torch.from_numpy(np.ascontiguousarray(q2k, dtype=np.int32)).to(dev)
-    O, LSE = m.forward(Q, K, V, q, SCALE)
+    O, LSE = m.forward(Q, K, V, q, scale)
     out = dict(O=O, LSE=LSE)
     if backward:
-        dQ, dK, dV = m.backward(Q, dO, O, LSE, SCALE)
+        dQ, dK, dV = m.backward(Q, dO, O, LSE, scale)
         out.update(dQ=dQ, dK=dK, dV=dV, delta=m.delta)
     torch.cuda.synchronize()
     return m, out

@@ -84,6 +84,23 @@ def test_backward_parity_grids(grid):
     check_close("dV", to_np(out["dV"]), dV)
 
 
+@pytest.mark.parametrize("scale", [0.03, 0.3])
+def test_parity_other_scales(scale):
+    """Softmax scales other than 1/sqrt(128): the scale enters the exponents, the dK
+    flush and the dQ epilogue separately."""
+    say("case sink_1000 scale", scale)
+    cu, q2k, tens = _small("sink_1000", scatter=True)
+    m, out = run_gpu(cu, q2k, tens, mode=3, scale=scale)
+    Q, K, V, dO = inputs64(tens)
+    O, LSE = OR.forward(Q, K, V, q2k, cu, scale)
+    check_close("O", to_np(out["O"]), O)
+    check_lse(to_np(out["LSE"]), LSE)
+    dQ, dK, dV, _, _ = OR.backward(Q, K, V, dO, q2k, cu, scale)
+    check_close("dQ", to_np(out["dQ"]), dQ)
+    check_close("dK", to_np(out["dK"]), dK)
+    check_close("dV", to_np(out["dV"]), dV)
+
+
 def test_invalid_ids_flagged_and_ignored():
     """Out-of-range and repeated ids set the status bits and add no keys."""
     cu, q2k, tens = _small("uniform_3docs_ragged")
