@@ -2,6 +2,8 @@
 // the host, then kernel launches on the caller's stream.
 #include <string.h>
 
+#include <atomic>
+
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -43,16 +45,20 @@ int check_layout(const msa_layout *L, LayoutArgs *out) {
 
 // The kernels are built for gfx950 only.
 int check_device() {
-  static int checked[64];  // 0 unknown, 1 ok, 2 bad
+  static std::atomic<int> checked[64];  // per device: 0 unknown, 1 ok, 2 bad (any thread)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MSA_ERR_DEVICE;
-  if (dev < 64 && checked[dev]) return checked[dev] == 1 ? MSA_OK : MSA_ERR_DEVICE;
+  const int known = dev < 64 ? checked[dev].load(std::memory_order_relaxed) : 0;
+  if (known) return known == 1 ? MSA_OK : MSA_ERR_DEVICE;
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MSA_ERR_DEVICE;
   int ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  if (dev < 64) checked[dev] = ok ? 1 : 2;
+  if (dev < 64) checked[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
   return ok ? MSA_OK : MSA_ERR_DEVICE;
 }
+
+// The softmax scale: finite and positive.
+bool scale_ok(float scale) { return scale > 0.f && scale < __builtin_inff(); }
 
 int launch_rc(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH; }
 
@@ -184,7 +190,7 @@ int msa_forward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vt, const
   int rc = check_layout(layout, &L);
   if (!rc) rc = check_ptrs({Q, Kw, Vt, q2k, plan, O, LSE});
   if (rc) return rc;
-  if (!(scale > 0.f) || scale != scale) return MSA_ERR_SHAPE;
+  if (!scale_ok(scale)) return MSA_ERR_SHAPE;
   if ((rc = check_device())) return rc;
   hipError_t e = mark(0, (hipStream_t)stream);
   if (e == hipSuccess) e = host::forward(Q, Kw, Vt, q2k, L, plan, scale, O, LSE, (hipStream_t)stream);
@@ -226,7 +232,7 @@ int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, cons
   if (dq_accum_mode != MSA_DQ_ACCUM_FP32 && dq_accum_mode != MSA_DQ_ACCUM_BF16X2 &&
       dq_accum_mode != MSA_DQ_RECOMPUTE && dq_accum_mode != MSA_DQ_STORED)
     return MSA_ERR_MODE;
-  if (!(scale > 0.f) || scale != scale) return MSA_ERR_SHAPE;
+  if (!scale_ok(scale)) return MSA_ERR_SHAPE;
   if (scratch_bytes < msa_bwd_scratch_bytes(layout, dq_accum_mode)) return MSA_ERR_SCRATCH;
   if ((rc = check_device())) return rc;
   hipStream_t s = (hipStream_t)stream;

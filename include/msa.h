@@ -177,7 +177,8 @@ int msa_plan(const msa_layout *layout, const int32_t *q2k, void *plan, size_t pl
 /* ---------------------------------------------------------------------------------
  * Forward (pull-request page, Design: Q[T,64,128], K/V, q2k -> O[T,64,128] + LSE).
  *   Q: bf16 [T, 64, 128].  Kw and Vt from msa_align_kv.  plan from msa_plan.  q2k as
- *   above.
+ *   above.  scale: the softmax scale applied to Q K^T, finite and > 0 (else
+ *   MSA_ERR_SHAPE).
  *   O: bf16 [T, 64, 128].  LSE: fp32 [T, 64], natural log of the sum of exp(scores),
  *   scores including `scale`; -inf (and O = 0) for a row with no keys.
  * --------------------------------------------------------------------------------- */
@@ -220,7 +221,8 @@ int msa_build_tasks(const msa_layout *layout, const int32_t *row_ptr, const int3
  *   Q, dO: bf16 [T, 64, 128]; Kw, Vw, Kt from msa_align_kv; LSE fp32 [T, 64] from
  *   msa_forward; delta from msa_backward_preprocess; q2k and plan as given to the
  *   forward; tasks from msa_build_tasks and `grid` the value it was built with (the
- *   KV-parallel launch uses that many workgroups).  Writes dQ bf16 [T, 64, 128] and
+ *   KV-parallel launch uses that many workgroups).  scale: the forward's softmax scale
+ *   (finite and > 0, else MSA_ERR_SHAPE).  Writes dQ bf16 [T, 64, 128] and
  *   dK, dV bf16 [T, 4, 128] in compact token order.  scratch >=
  *   msa_bwd_scratch_bytes(layout, dq_accum_mode): the dQ pool of the pooled modes and
  *   fp32 dK/dV pools, zeroed by this call, then (MSA_DQ_STORED) the dS tiles, 4 KiB per

@@ -95,6 +95,11 @@ def test_argument_errors_return_before_device_use(M):
     assert bw(0, 2, 1 << 40) == E["GRID"]
     assert bw(256, 0, 16) == E["SCRATCH"]
     assert bw(256, 2, 16) == E["SCRATCH"]
+    # the softmax scale must be finite and positive (checked before the device)
+    for sc in (0.0, -0.5, float("nan"), float("inf")):
+        assert lib.msa_forward(a, a, a, a, L.ref(), a, ctypes.c_float(sc), a, a, None) == E["SHAPE"], sc
+        assert lib.msa_backward(a, a, a, a, a, a, a, a, a, a, 256, L.ref(), ctypes.c_float(sc), 2, a, a, a, a,
+                                1 << 40, None) == E["SHAPE"], sc
     bad = FakeLayout(M, T=1000, W=1000)
     assert lib.msa_align_kv(a, a, bad.ref(), a, a, a, a, None) == E["SHAPE"]
     assert lib.msa_status_string(4) == b"buffer smaller than its size query"
