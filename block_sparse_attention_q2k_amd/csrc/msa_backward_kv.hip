@@ -127,6 +127,7 @@ struct KvState {
   f32x16 dkacc[4], dvacc[4];
   bf16x8 kf[8], vf[8];
   int cur_r, kbase, gb;
+  int r_row, nv_row;  // bucket and valid-query count of the row about to be computed
   float lse2, del;
   int pos, qt;  // qt: stored-dS tile index of the next row's query tid (tid < 8)
   int idv;      // ids of the next row (kv_ids_load)
@@ -146,8 +147,8 @@ __device__ __forceinline__ void kv_row(
   const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
   const int j16 = lane & 15, G = l32 >> 4;
   const lds_char *lcur = (const lds_char *)cur;
-  const i32x4 mt4 = meta[row];
-  const int r = mt4[0];
+  // this row's meta entry came with the previous row's ids (no scalar load to wait for)
+  const int r = st.r_row, nv = st.nv_row;
   // 1. new bucket: this wave's K/V slices (issued before the asynchronous gather so that
   //    waiting for them never waits for the gather)
   if (r != st.cur_r) {
@@ -249,7 +250,7 @@ __device__ __forceinline__ void kv_row(
         pa[e] = (__bf16)sacc[m2][8 * sg + e];
         sa[e] = (__bf16)pacc[m2][8 * sg + e];
       }
-      if (STORE_DS && 4 * half + k2 < mt4[1]) {
+      if (STORE_DS && 4 * half + k2 < nv) {
         // sa: query 4 half + k2, key 32 w + l32, heads 4 h .. + 3 and 8 + 4 h .. + 3,
         // which are tile positions 8 h .. 8 h + 7.  Streaming (non-temporal) store: the
         // tiles are read once, by the dQ kernel, and should not displace the Q/dO rows
@@ -289,6 +290,8 @@ __device__ __forceinline__ void kv_row(
   if (more && tid < 128) kv_store_scalars(nxt_sc, tid, st.lse2, st.del, st.pos);
   if (STORE_DS && more && tid < kTileQ) ((int32_t *)nxt_sc)[kKvScTile + tid] = st.qt;
   wait_vm();
+  st.r_row = r_next;
+  st.nv_row = __builtin_amdgcn_readlane(st.idv, 17);
   st.idv = idv2;
   __syncthreads();
 }
@@ -316,7 +319,10 @@ bwd_kv_kernel(uint16_t *__restrict__ dS, const int32_t *__restrict__ qtile,
     if (lo >= hi) continue;
     {  // prologue: row lo into tile 0
       KvRowIds ids;
-      kv_row_ids(ids, qrows, qpos, lo, meta[lo][1]);
+      const i32x4 m0 = meta[lo];
+      st.r_row = m0[0];
+      st.nv_row = m0[1];
+      kv_row_ids(ids, qrows, qpos, lo, m0[1]);
       st.idv = lo + 1 < hi ? kv_ids_load(qrows, qpos, meta, lo + 1, tid & 63) : 0;
       if (tid < 128) {
         kv_scalars(LSE, Delta, ids, i, tid, st.lse2, st.del, st.pos);
