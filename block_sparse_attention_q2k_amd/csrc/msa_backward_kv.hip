@@ -68,11 +68,16 @@ __device__ __forceinline__ int kv_ids_load(const int32_t *__restrict__ qrows, co
                                    : (const int32_t *)(meta + row) + ((lane - 16) & 3);
   return lane < 20 ? *src : 0;
 }
-__device__ __forceinline__ void kv_ids_unpack(KvRowIds &ids, int v, int nv) {
+// Padding queries (k >= nv) take query 0's id and position -1; the selection is made
+// once in the vector register, so that every id leaves it by a constant-lane readlane.
+__device__ __forceinline__ void kv_ids_unpack(KvRowIds &ids, int v, int nv, int lane) {
+  const int v0 = __builtin_amdgcn_readlane(v, 0);
+  const bool pad = (lane & 7) >= nv;
+  const int u = lane < 8 ? (pad ? v0 : v) : lane < 16 ? (pad ? -1 : v) : v;
 #pragma unroll
   for (int k = 0; k < kTileQ; ++k) {
-    ids.t[k] = __builtin_amdgcn_readlane(v, k < nv ? k : 0);
-    ids.pos[k] = k < nv ? __builtin_amdgcn_readlane(v, 8 + k) : -1;
+    ids.t[k] = __builtin_amdgcn_readlane(u, k);
+    ids.pos[k] = __builtin_amdgcn_readlane(u, 8 + k);
   }
 }
 
@@ -178,7 +183,7 @@ __device__ __forceinline__ void kv_row(
   const int idv2 = row + 2 < hi ? kv_ids_load(qrows, qpos, meta, row + 2, lane) : 0;
   KvRowIds ids;
   if (more) {
-    kv_ids_unpack(ids, st.idv, __builtin_amdgcn_readlane(st.idv, 17));
+    kv_ids_unpack(ids, st.idv, __builtin_amdgcn_readlane(st.idv, 17), lane);
     if (tid < 128) kv_scalars(LSE, Delta, ids, i, tid, st.lse2, st.del, st.pos);
     if (STORE_DS && tid < kTileQ) st.qt = qtile[(size_t)(row + 1) * kTileQ + tid];
   }
