@@ -318,25 +318,40 @@ plan_groups_kernel(const int32_t *__restrict__ cu, int ndocs, int Gmax, int32_t 
   }
 }
 
+// Cost (member slots) and {t0, n, doc} of every (index head, query group) of the plan.
 __global__ void plan_cost_kernel(const int32_t *__restrict__ q2k, const int32_t *__restrict__ cu,
                                  int ndocs, int T, int Gmax, const int32_t *__restrict__ plan,
                                  const int32_t *__restrict__ gstart, i32x4 *__restrict__ ginfo,
                                  int32_t *__restrict__ cost) {
-  int gid = blockIdx.x * blockDim.x + threadIdx.x;
-  int G = plan[1];
-  if (gid >= kHI * G) return;
-  int i = gid / G, g = gid - i * G;
-  int d = upper_index(gstart, ndocs - 1, g);
-  int t0 = cu[d] + (g - gstart[d]) * kFwdGroup;
-  int n = min(kFwdGroup, cu[d + 1] - t0);
-  int c = 0, flags = 0;
-  int32_t ids[kTopk];
-  for (int u = 0; u < n; ++u) {
-    int t = t0 + u;
-    c += __popc(member_mask(q2k + ((size_t)i * T + t) * kTopk, (t - cu[d]) / kBlk, ids, &flags));
+  // 16 lanes (a quarter wave) per (index head, group), one per query; the group's cost is
+  // their sum.  No lane returns early: all 16 take part in the sum.
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int G = plan[1];
+  const int team = gid >> 4, u = gid & 15;
+  const bool valid = team < kHI * G;
+  int c = 0, i = 0, g = 0, d = 0, t0 = 0, n = 0;
+  if (valid) {
+    i = team / G;
+    g = team - i * G;
+    d = upper_index(gstart, ndocs - 1, g);
+    t0 = cu[d] + (g - gstart[d]) * kFwdGroup;
+    n = min(kFwdGroup, cu[d + 1] - t0);
+    if (u < n) {
+      int32_t ids[kTopk];
+      int flags = 0;
+      const int t = t0 + u;
+      c = __popc(member_mask(q2k + ((size_t)i * T + t) * kTopk, (t - cu[d]) / kBlk, ids, &flags));
+    }
   }
-  cost[i * Gmax + g] = c;
-  if (i == 0) ginfo[g] = i32x4{t0, n, d, 0};
+  static_assert(kFwdGroup == 16, "one quarter wave per group");
+  c += __shfl_xor(c, 8, 16);
+  c += __shfl_xor(c, 4, 16);
+  c += __shfl_xor(c, 2, 16);
+  c += __shfl_xor(c, 1, 16);
+  if (valid && u == 0) {
+    cost[i * Gmax + g] = c;
+    if (i == 0) ginfo[g] = i32x4{t0, n, d, 0};
+  }
 }
 
 // One workgroup per index head: stable counting sort of its groups by cost,
@@ -597,7 +612,7 @@ hipError_t build_plan(const LayoutArgs &L, const int32_t *q2k, void *plan_v, hip
   const int gmax = (int)plan_gmax(L);
   hipLaunchKernelGGL(plan_groups_kernel, dim3(1), dim3(1024), 0, s, L.cu, L.ndocs, gmax, v.header,
                      v.gstart);
-  hipLaunchKernelGGL(plan_cost_kernel, dim3(blocks_for((size_t)kHI * gmax, 128)), dim3(128), 0, s,
+  hipLaunchKernelGGL(plan_cost_kernel, dim3(blocks_for((size_t)kHI * gmax * 16, 256)), dim3(256), 0, s,
                      q2k, L.cu, L.ndocs, L.T, gmax, v.header, v.gstart, (i32x4 *)v.ginfo, v.cost);
   hipLaunchKernelGGL(plan_sort_kernel, dim3(kHI), dim3(1024), 0, s, gmax, v.header,
                      (const i32x4 *)v.ginfo, v.cost);
