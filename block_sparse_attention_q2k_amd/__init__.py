@@ -93,6 +93,35 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _need(fn, name, t, dtype, shape=None, min_numel=None):
+    """The C ABI sees only pointers, so a tensor of the wrong size would be read or written
+    past its end on the GPU: require a contiguous tensor of this dtype and exact shape (or at
+    least min_numel elements).  (The device is checked by _gpu, after all of these.)"""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s: %s must be a torch tensor" % (fn, name))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s: %s has dtype %s, expected %s" % (fn, name, t.dtype, dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: %s has shape %s, expected %s" % (fn, name, tuple(t.shape), tuple(shape)))
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError("%s: %s has %d elements, needs at least %d" % (fn, name, t.numel(), min_numel))
+    if not t.is_contiguous():
+        raise ValueError("%s: %s is not contiguous" % (fn, name))
+
+
+def _gpu(fn, **tensors):
+    """After the structural checks: every tensor argument must live on a GPU."""
+    for name, t in tensors.items():
+        if not t.is_cuda:
+            raise ValueError("%s: %s is not on a GPU" % (fn, name))
+
+
+def _dt():
+    import torch
+    return torch.bfloat16, torch.float32, torch.int32, torch.uint8
+
+
 def _stream(stream):
     import torch
     if stream is None:
@@ -158,33 +187,77 @@ def msa_tasks_meta_offset(grid):
 
 
 def msa_align_kv(K, V, layout, Kw, Vw, Kt, Vt, stream=None):
+    bf, _, _, _ = _dt()
+    for n, t in (("K", K), ("V", V)):
+        _need("msa_align_kv", n, t, bf, (layout.T, NUM_KV_HEADS, HEAD_DIM))
+    for n, t in (("Kw", Kw), ("Vw", Vw), ("Kt", Kt), ("Vt", Vt)):
+        _need("msa_align_kv", n, t, bf, min_numel=layout.W * NUM_KV_HEADS * HEAD_DIM)
+    _gpu("msa_align_kv", K=K, V=V, Kw=Kw, Vw=Vw, Kt=Kt, Vt=Vt)
     _check("msa_align_kv", lib().msa_align_kv(_ptr(K), _ptr(V), layout.ref(), _ptr(Kw), _ptr(Vw),
                                               _ptr(Kt), _ptr(Vt), _stream(stream)))
 
 
+def _need_q2k(fn, q2k, layout):
+    _need(fn, "q2k", q2k, _dt()[2], (NUM_INDEX_HEADS, layout.T, TOPK))
+
+
 def msa_build_k2q_csr(q2k, layout, row_ptr, cols, status, scratch, stream=None):
+    _, _, i32, _ = _dt()
+    fn = "msa_build_k2q_csr"
+    _need_q2k(fn, q2k, layout)
+    _need(fn, "row_ptr", row_ptr, i32, min_numel=NUM_INDEX_HEADS * layout.NB + 1)
+    _need(fn, "cols", cols, i32, min_numel=msa_csr_cols_capacity(layout))
+    _need(fn, "status", status, i32, min_numel=1)
+    _need(fn, "scratch", scratch, None)
+    _gpu(fn, q2k=q2k, row_ptr=row_ptr, cols=cols, status=status, scratch=scratch)
     _check("msa_build_k2q_csr", lib().msa_build_k2q_csr(
         _ptr(q2k), layout.ref(), _ptr(row_ptr), _ptr(cols), _ptr(status), _ptr(scratch),
         scratch.numel() * scratch.element_size(), _stream(stream)))
 
 
 def msa_plan(layout, q2k, plan, stream=None):
+    _need_q2k("msa_plan", q2k, layout)
+    _need("msa_plan", "plan", plan, None)
+    _gpu("msa_plan", q2k=q2k, plan=plan)
     _check("msa_plan", lib().msa_plan(layout.ref(), _ptr(q2k), _ptr(plan),
                                       plan.numel() * plan.element_size(), _stream(stream)))
 
 
 def msa_forward(Q, Kw, Vt, q2k, layout, plan, scale, O, LSE, stream=None):
+    bf, f32, _, _ = _dt()
+    fn = "msa_forward"
+    for n, t in (("Q", Q), ("O", O)):
+        _need(fn, n, t, bf, (layout.T, NUM_Q_HEADS, HEAD_DIM))
+    for n, t in (("Kw", Kw), ("Vt", Vt)):
+        _need(fn, n, t, bf, min_numel=layout.W * NUM_KV_HEADS * HEAD_DIM)
+    _need(fn, "LSE", LSE, f32, (layout.T, NUM_Q_HEADS))
+    _need_q2k(fn, q2k, layout)
+    _need(fn, "plan", plan, None, min_numel=msa_plan_bytes(layout) // plan.element_size())
+    _gpu(fn, Q=Q, Kw=Kw, Vt=Vt, q2k=q2k, plan=plan, O=O, LSE=LSE)
     _check("msa_forward", lib().msa_forward(_ptr(Q), _ptr(Kw), _ptr(Vt), _ptr(q2k), layout.ref(),
                                             _ptr(plan), float(scale), _ptr(O), _ptr(LSE),
                                             _stream(stream)))
 
 
 def msa_backward_preprocess(O, dO, num_tokens, delta, stream=None):
+    bf, f32, _, _ = _dt()
+    fn = "msa_backward_preprocess"
+    for n, t in (("O", O), ("dO", dO)):
+        _need(fn, n, t, bf, (int(num_tokens), NUM_Q_HEADS, HEAD_DIM))
+    _need(fn, "delta", delta, f32, (int(num_tokens), NUM_Q_HEADS))
+    _gpu(fn, O=O, dO=dO, delta=delta)
     _check("msa_backward_preprocess", lib().msa_backward_preprocess(
         _ptr(O), _ptr(dO), int(num_tokens), _ptr(delta), _stream(stream)))
 
 
 def msa_build_tasks(layout, row_ptr, cols, q2k, grid, tasks, stream=None):
+    _, _, i32, _ = _dt()
+    fn = "msa_build_tasks"
+    _need(fn, "row_ptr", row_ptr, i32, min_numel=NUM_INDEX_HEADS * layout.NB + 1)
+    _need(fn, "cols", cols, i32, min_numel=msa_csr_cols_capacity(layout))
+    _need_q2k(fn, q2k, layout)
+    _need(fn, "tasks", tasks, None)
+    _gpu(fn, row_ptr=row_ptr, cols=cols, q2k=q2k, tasks=tasks)
     _check("msa_build_tasks", lib().msa_build_tasks(layout.ref(), _ptr(row_ptr), _ptr(cols), _ptr(q2k),
                                                     int(grid), _ptr(tasks), tasks.numel() * tasks.element_size(),
                                                     _stream(stream)))
@@ -192,6 +265,22 @@ def msa_build_tasks(layout, row_ptr, cols, q2k, grid, tasks, stream=None):
 
 def msa_backward(Q, Kw, Vw, Kt, dO, LSE, delta, q2k, plan, tasks, grid, layout, scale, mode, dQ, dK,
                  dV, scratch, stream=None):
+    bf, f32, _, _ = _dt()
+    fn = "msa_backward"
+    for n, t in (("Q", Q), ("dO", dO), ("dQ", dQ)):
+        _need(fn, n, t, bf, (layout.T, NUM_Q_HEADS, HEAD_DIM))
+    for n, t in (("Kw", Kw), ("Vw", Vw), ("Kt", Kt)):
+        _need(fn, n, t, bf, min_numel=layout.W * NUM_KV_HEADS * HEAD_DIM)
+    for n, t in (("dK", dK), ("dV", dV)):
+        _need(fn, n, t, bf, (layout.T, NUM_KV_HEADS, HEAD_DIM))
+    for n, t in (("LSE", LSE), ("delta", delta)):
+        _need(fn, n, t, f32, (layout.T, NUM_Q_HEADS))
+    _need_q2k(fn, q2k, layout)
+    _need(fn, "plan", plan, None, min_numel=msa_plan_bytes(layout) // plan.element_size())
+    _need(fn, "tasks", tasks, None, min_numel=msa_tasks_bytes(layout, int(grid)) // tasks.element_size())
+    _need(fn, "scratch", scratch, None)
+    _gpu(fn, Q=Q, Kw=Kw, Vw=Vw, Kt=Kt, dO=dO, LSE=LSE, delta=delta, q2k=q2k, plan=plan, tasks=tasks,
+         dQ=dQ, dK=dK, dV=dV, scratch=scratch)
     _check("msa_backward", lib().msa_backward(
         _ptr(Q), _ptr(Kw), _ptr(Vw), _ptr(Kt), _ptr(dO), _ptr(LSE), _ptr(delta), _ptr(q2k),
         _ptr(plan), _ptr(tasks), int(grid),
@@ -267,6 +356,8 @@ class MSA:
             dK = torch.empty((L.T, NUM_KV_HEADS, HEAD_DIM), dtype=torch.bfloat16, device=self.device)
         if dV is None:
             dV = torch.empty_like(dK)
+        if not hasattr(self, "q2k"):
+            raise RuntimeError("MSA.backward needs the CSR, plan and workspace of a forward call first")
         msa_backward_preprocess(O, dO, L.T, self.delta, stream)
         msa_build_tasks(L, self.row_ptr, self.cols, self.q2k, self.grid, self.tasks, stream)
         msa_backward(Q, self.Kw, self.Vw, self.Kt, dO, LSE, self.delta, self.q2k, self.plan,

@@ -105,6 +105,41 @@ def test_argument_errors_return_before_device_use(M):
     assert lib.msa_status_string(4) == b"buffer smaller than its size query"
 
 
+def test_binding_refuses_tensors_the_kernels_would_overrun(M):
+    """The binding checks dtype, shape, contiguity and device before any pointer reaches the
+    library (which sees only pointers)."""
+    import torch
+    L = M.Layout([0, 300, 700], device="cpu")
+    T, W = L.T, L.W
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    Q = torch.zeros((T, 64, 128), dtype=bf)
+    Kw = torch.zeros((W, 4, 128), dtype=bf)
+    q2k = torch.full((4, T, 16), -1, dtype=i32)
+    plan = torch.zeros(M.msa_plan_bytes(L), dtype=torch.uint8)
+    LSE = torch.zeros((T, 64), dtype=f32)
+    call = lambda **kw: M.msa_forward(**{**dict(Q=Q, Kw=Kw, Vt=Kw, q2k=q2k, layout=L, plan=plan, scale=0.1,
+                                                O=Q, LSE=LSE), **kw})
+    with pytest.raises(ValueError, match="dtype"):
+        call(Q=Q.float())
+    with pytest.raises(ValueError, match="shape"):
+        call(O=torch.zeros((T - 1, 64, 128), dtype=bf))
+    with pytest.raises(ValueError, match="shape"):
+        call(q2k=torch.full((4, T, 8), -1, dtype=i32))
+    with pytest.raises(ValueError, match="at least"):
+        call(Kw=torch.zeros((W - 128, 4, 128), dtype=bf))
+    with pytest.raises(ValueError, match="contiguous"):
+        call(Q=torch.zeros((64, T, 128), dtype=bf).transpose(0, 1))
+    with pytest.raises(ValueError, match="not on a GPU"):
+        call()
+    with pytest.raises(TypeError):
+        call(LSE=np.zeros((T, 64), dtype=np.float32))
+    with pytest.raises(ValueError, match="shape"):
+        M.msa_backward_preprocess(Q, Q, T, torch.zeros((T, 63), dtype=f32))
+    m = M.MSA([0, 300, 700], grid=8, device="cpu")
+    with pytest.raises(RuntimeError, match="forward"):
+        m.backward(Q, Q, Q, LSE, 0.1)
+
+
 def test_product_path_has_no_oracle_dependency():
     """The package neither imports nor loads anything under oracle/."""
     pkg = os.path.join(ROOT, "block_sparse_attention_q2k_amd")
