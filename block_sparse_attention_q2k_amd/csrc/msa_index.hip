@@ -225,42 +225,66 @@ plan_lists_kernel(const int32_t *__restrict__ q2k, const int32_t *__restrict__ c
   const int i = it[0], t0 = it[1], n = it[2], d = it[3];
   const int p0 = t0 - cu[d];
   constexpr int kNone = 0x7fffffff;
-#pragma unroll
-  for (int h = 0; h < kPer; ++h) {
-    const int e = tid + kListThreads * h, u = e >> 4, j = e & 15;
-    int key = kNone;
-    if (u < n) {  // n <= kFwdGroup, so e < kPlanMaxList
-      const int b = q2k[((size_t)i * T + t0 + u) * kTopk + j];
-      if (b >= 0 && b <= (p0 + u) / kBlk) key = (b << 5) | u;
-    }
-    keys[e] = key;
-  }
-  __syncthreads();
-  for (int k = 2; k <= kSortN; k <<= 1)
-    for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      {  // kSortN / 2 compare pairs, one per thread
-        const int q = tid;
-        const int a = (q / jj) * 2 * jj + (q % jj), b = a + jj;
-        const int ka = keys[a], kb = keys[b];
-        const bool up = (a & k) == 0;
-        if ((ka > kb) == up) {
-          keys[a] = kb;
-          keys[b] = ka;
-        }
-      }
-      __syncthreads();
-    }
   int start[kPer], mask[kPer], blk[kPer];
+  // The item's queries can only select blocks 0 .. nblk - 1.  Up to kSortN of them (64k-token
+  // documents): one query-bit mask per block in LDS, OR-ed together; else the sort below.
+  const int nblk = (p0 + n - 1) / kBlk + 1;
+  if (nblk <= kSortN) {
+    for (int b = tid; b < nblk; b += kListThreads) keys[b] = 0;
+    __syncthreads();
 #pragma unroll
-  for (int h = 0; h < kPer; ++h) {
-    const int e = tid * kPer + h;  // consecutive keys per thread keep the runs in order
-    const int key = keys[e];
-    blk[h] = key >> 5;
-    start[h] = key != kNone && (e == 0 || (keys[e - 1] >> 5) != blk[h]);
-    mask[h] = 0;
-    if (start[h])
-      for (int f = e; f < kSortN && keys[f] != kNone && (keys[f] >> 5) == blk[h]; ++f)
-        mask[h] |= 1 << (keys[f] & 31);
+    for (int h = 0; h < kPer; ++h) {
+      const int e = tid + kListThreads * h, u = e >> 4, j = e & 15;
+      if (u < n) {
+        const int b = q2k[((size_t)i * T + t0 + u) * kTopk + j];
+        if (b >= 0 && b <= (p0 + u) / kBlk) atomicOr(&keys[b], 1 << u);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < kPer; ++h) {
+      const int b = tid * kPer + h;  // consecutive blocks per thread keep the list in order
+      blk[h] = b;
+      mask[h] = b < nblk ? keys[b] : 0;
+      start[h] = mask[h] != 0;
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < kPer; ++h) {
+      const int e = tid + kListThreads * h, u = e >> 4, j = e & 15;
+      int key = kNone;
+      if (u < n) {  // n <= kFwdGroup, so e < kPlanMaxList
+        const int b = q2k[((size_t)i * T + t0 + u) * kTopk + j];
+        if (b >= 0 && b <= (p0 + u) / kBlk) key = (b << 5) | u;
+      }
+      keys[e] = key;
+    }
+    __syncthreads();
+    for (int k = 2; k <= kSortN; k <<= 1)
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        {  // kSortN / 2 compare pairs, one per thread
+          const int q = tid;
+          const int a = (q / jj) * 2 * jj + (q % jj), b = a + jj;
+          const int ka = keys[a], kb = keys[b];
+          const bool up = (a & k) == 0;
+          if ((ka > kb) == up) {
+            keys[a] = kb;
+            keys[b] = ka;
+          }
+        }
+        __syncthreads();
+      }
+#pragma unroll
+    for (int h = 0; h < kPer; ++h) {
+      const int e = tid * kPer + h;  // consecutive keys per thread keep the runs in order
+      const int key = keys[e];
+      blk[h] = key >> 5;
+      start[h] = key != kNone && (e == 0 || (keys[e - 1] >> 5) != blk[h]);
+      mask[h] = 0;
+      if (start[h])
+        for (int f = e; f < kSortN && keys[f] != kNone && (keys[f] >> 5) == blk[h]; ++f)
+          mask[h] |= 1 << (keys[f] & 31);
+    }
   }
   int mine = 0;
 #pragma unroll

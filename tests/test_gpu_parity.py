@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import block_sparse_attention_q2k_amd as M
 import workloads as WL
 from oracle import oracle as OR
 from _gpu_util import (SCALE, check_close, check_lse, check_structures, inputs64, run_gpu, say,
@@ -31,6 +32,29 @@ def _small(name, scatter=False):
         q2k = WL.scatter_unused(q2k, seed)
     tens = WL.make_tensors(int(cu[-1]), 100 + seed)
     return cu, q2k, tens
+
+
+def test_plan_long_document():
+    """Walk lists of a 70,000-token document (547 blocks: items past 512 blocks take the
+    sorting list builder, the others the per-block mask builder) and a short one, bit-exact
+    against the oracle's plan."""
+    say("case", "plan_70000_3000")
+    cu, q2k = WL.make_custom([70000, 3000], "uniform", 11)
+    dev = "cuda:0"
+    m = M.MSA(cu, device=dev)
+    q = torch.from_numpy(np.ascontiguousarray(q2k, dtype=np.int32)).to(dev)
+    M.msa_build_k2q_csr(q, m.layout, m.row_ptr, m.cols, m.status, m.csr_scratch)
+    M.msa_plan(m.layout, q, m.plan)
+    torch.cuda.synchronize()
+    items, lists = m.plan_items()
+    oitems, _, olists = OR.forward_plan(q2k, cu, m.fwd_group)
+    np.testing.assert_array_equal(items, oitems)
+    assert len(lists) == len(olists)
+    long_items = 0
+    for it, a, b in zip(items, lists, olists):
+        np.testing.assert_array_equal(a, b)
+        long_items += (int(it[1]) - int(cu[int(it[3])]) + int(it[2]) - 1) // 128 + 1 > 512
+    assert long_items > 0
 
 
 @pytest.mark.parametrize("name", list(SMALL))
