@@ -302,9 +302,10 @@ __device__ __forceinline__ void fwd_step(const FwdCtx &x, int a, FwdPos &q, cons
     return;
   }
   // The next block's operands are requested in four groups of four loads spread over
-  // the step (K rows before and after the S phase, V^T slices before and after the PV
-  // phase): issued together right after a barrier, the loads of all waves queue up and
-  // stall the waves' instruction streams until they are accepted.
+  // the step (the K rows at the start and before the S phase, so that they have a whole
+  // step to arrive; the V^T slices before and after the PV phase): issued together right
+  // after a barrier, the loads of all waves queue up and stall the waves' instruction
+  // streams until they are accepted.
   fwd_load_k_half<0>(x, kn, q.bn);
   fwd_pos_fetch(x, q, a);
   WAIT_VMCNT(12);  // this step's K rows (issued in the previous step)
@@ -313,8 +314,8 @@ __device__ __forceinline__ void fwd_step(const FwdCtx &x, int a, FwdPos &q, cons
   if (fresh) fwd_references(x, kc, fresh, b);
   seen |= m;
   // ---- S phase: the step's units in pairs, this wave's keys (one slot per unit)
-  fwd_scores(x, kc, m, b, dmask);
   fwd_load_k_half<1>(x, kn, q.bn);
+  fwd_scores(x, kc, m, b, dmask);
   lds_barrier();
   fwd_load_v_half<0>(x, vn, q.bn);
   WAIT_VMCNT(12);  // this step's V^T slices
