@@ -1,5 +1,5 @@
-"""GPU parity at the five workloads' full sizes, in the launch configuration the
-benchmark times (default grid = one workgroup per CU).  Integer structures are
+"""GPU parity at the five workloads' full sizes and on one long document, in the
+launch configuration the benchmark times (default grid = one workgroup per CU).  Integer structures are
 compared in full; O, LSE and dQ on a seeded sample of query rows the oracle computes
 one by one; dK/dV on sampled key blocks whose selecting queries the oracle enumerates
 in full; at every row, finiteness and delta = rowsum(dO * O)."""
@@ -55,12 +55,23 @@ def _rows64(x, rows):
     return out
 
 
+# One document of 547 key blocks (past the 512-block point where the plan builder
+# switches from its block bitmap to sorting the item's entries) and a short one.
+LONG = "long"
+
+
+def _structure(cfg):
+    if cfg == LONG:
+        return WL.make_custom([70000, 3000], "uniform", 11), 100
+    return WL.make_structure(cfg), cfg
+
+
 @functools.lru_cache(maxsize=1)
 def _case(cfg):
     say("  generating workload", cfg)
-    cu, q2k = WL.make_structure(cfg)
-    tens = WL.make_tensors(int(cu[-1]), 1000 + cfg)
-    rng = np.random.default_rng(77 + cfg)
+    (cu, q2k), seed = _structure(cfg)
+    tens = WL.make_tensors(int(cu[-1]), 1000 + seed)
+    rng = np.random.default_rng(77 + seed)
     qmask = _sample_rows(cu, rng)
     kmask, selectors, blocks = _sample_blocks(cu, q2k, rng)
     need = qmask | selectors
@@ -74,7 +85,7 @@ def _case(cfg):
 
 
 @pytest.mark.parametrize("mode", [3, 2])
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, LONG])
 def test_full_size_config(cfg, mode):
     say("config", cfg, "dq mode", mode)
     cu, q2k, tens, qmask, kmask, ref = _case(cfg)
