@@ -64,9 +64,10 @@ int launch_rc(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH; 
 
 size_t round16(size_t b) { return (b + 15) / 16 * 16; }
 
-// Stored dS tiles: T x 4 index heads x 16 slots x (16 heads x 128 keys) bf16.
+// Stored dS tiles: T x 4 index heads x 16 slots x (16 heads x 128 keys) bf16, plus one
+// spare tile that the KV-parallel kernel writes for the padding queries of a task row.
 size_t ds_store_bytes(const LayoutArgs &L) {
-  return (size_t)L.T * MSA_NUM_INDEX_HEADS * MSA_TOPK * 16 * MSA_BLOCK * 2;
+  return ((size_t)L.T * MSA_NUM_INDEX_HEADS * MSA_TOPK + 1) * 16 * MSA_BLOCK * 2;
 }
 
 thread_local hipEvent_t t_events[MSA_TIMING_EVENTS] = {};

@@ -1,8 +1,18 @@
 """GPU parity at the five workloads' full sizes and on one long document, in the
-launch configuration the benchmark times (default grid = one workgroup per CU).  Integer structures are
-compared in full; O, LSE and dQ on a seeded sample of query rows the oracle computes
-one by one; dK/dV on sampled key blocks whose selecting queries the oracle enumerates
-in full; at every row, finiteness and delta = rowsum(dO * O)."""
+launch configuration the benchmark times (default grid = one workgroup per CU).
+
+* The 512-token document and the headline 16384-token document are compared in full:
+  every element of O, LSE, dQ, dK and dV against the oracle run over the whole
+  workload, in every dQ mode.  The sink block of the headline workload (selected by
+  every query: 2048 task rows per index head, split over many workgroups whose fp32
+  flushes all land on its 128 keys) is reported on its own.
+* The other workloads: integer structures in full; O, LSE and dQ on a seeded sample of
+  query rows the oracle computes one by one; dK/dV on the three most-selected key blocks
+  (the largest buckets, whose rows are split over the most workgroups) plus two random
+  ones, whose selecting queries the oracle enumerates in full.  The 4 x 16384-token
+  batch of short documents (Zipf-skewed picks, the workload that concentrates atomic
+  traffic) also runs the two pooled dQ modes.
+* At every row: finiteness, and delta = rowsum(dO * O)."""
 import functools
 
 import numpy as np
@@ -15,6 +25,9 @@ from _gpu_util import SCALE, check_close, check_lse, check_structures, run_gpu, 
 
 pytestmark = pytest.mark.gpu
 
+# dQ modes of the library: 0 fp32 pool, 1 packed-bf16 pool, 2 recompute, 3 stored dS
+STORED, RECOMPUTE, POOL_FP32, POOL_BF16X2 = 3, 2, 0, 1
+
 
 def _sample_rows(cu, rng, n=40):
     T = int(cu[-1])
@@ -25,14 +38,16 @@ def _sample_rows(cu, rng, n=40):
     return mask
 
 
-def _sample_blocks(cu, q2k, rng, n=2, max_queries=1000):
-    """Key tokens of n random workspace blocks that at most max_queries (index head,
-    query) pairs select (keeps the oracle's enumeration bounded)."""
+def _sample_blocks(cu, q2k, rng, n_random=2, n_heavy=3, max_queries=1000):
+    """Key tokens of the n_heavy most-selected workspace blocks (summed over the index
+    heads) plus n_random blocks that at most max_queries (index head, query) pairs
+    select.  Returns (key-token mask, mask of the queries selecting them, blocks)."""
     row_ptr, cols = OR.k2q_csr(q2k, cu)
     cu_ws, W, NB = OR.layout(cu)
     counts = np.diff(row_ptr).reshape(4, NB).sum(0)
-    ok = np.nonzero((counts > 0) & (counts <= max_queries))[0]
-    pick = rng.choice(ok, size=min(n, len(ok)), replace=False)
+    heavy = [int(b) for b in np.argsort(-counts, kind="stable")[:n_heavy]]
+    ok = np.setdiff1d(np.nonzero((counts > 0) & (counts <= max_queries))[0], heavy)
+    pick = heavy + [int(b) for b in rng.choice(ok, size=min(n_random, len(ok)), replace=False)]
     T = int(cu[-1])
     doc, pos, _ = OR.coords(cu)
     ws_row = cu_ws[doc] + pos
@@ -75,7 +90,7 @@ def _case(cfg):
     qmask = _sample_rows(cu, rng)
     kmask, selectors, blocks = _sample_blocks(cu, q2k, rng)
     need = qmask | selectors
-    say("  oracle: rows", int(qmask.sum()), "key blocks", list(blocks), "rows read", int(need.sum()))
+    say("  oracle: rows", int(qmask.sum()), "key blocks", blocks, "rows read", int(need.sum()))
     Q, dO = _rows64(tens["Q"], need), _rows64(tens["dO"], need)
     K, V = (tens[k].float().numpy().astype(np.float64) for k in ("K", "V"))
     rO, rL = OR.forward(Q, K, V, q2k, cu, SCALE, rows=qmask)
@@ -84,8 +99,57 @@ def _case(cfg):
     return cu, q2k, tens, qmask, kmask, ref
 
 
-@pytest.mark.parametrize("mode", [3, 2])
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, LONG])
+@functools.lru_cache(maxsize=1)
+def _full_case(cfg):
+    """The whole workload through the oracle (every row, every key)."""
+    say("  generating workload", cfg, "(every element)")
+    cu, q2k = WL.make_structure(cfg)
+    tens = WL.make_tensors(int(cu[-1]), 1000 + cfg)
+    Q, K, V, dO = (tens[k].float().numpy().astype(np.float64) for k in ("Q", "K", "V", "dO"))
+    say("  oracle: forward and backward over all", int(cu[-1]), "tokens")
+    rO, rL = OR.forward(Q, K, V, q2k, cu, SCALE)
+    rdQ, rdK, rdV, _, _ = OR.backward(Q, K, V, dO, q2k, cu, SCALE)
+    say("  oracle done")
+    return cu, q2k, tens, dict(O=rO, LSE=rL, dQ=rdQ, dK=rdK, dV=rdV)
+
+
+def _check_common(out, tens):
+    for k in ("O", "dQ", "dK", "dV"):
+        assert torch.isfinite(out[k].float()).all(), k
+    d_ref = (out["O"].float() * tens["dO"].cuda().float()).sum(-1)
+    assert torch.allclose(out["delta"], d_ref, rtol=1e-4, atol=1e-4)
+
+
+@pytest.mark.parametrize("mode", [STORED, RECOMPUTE, POOL_FP32, POOL_BF16X2])
+@pytest.mark.parametrize("cfg", [0, 2])
+def test_full_size_every_element(cfg, mode):
+    say("config", cfg, "dq mode", mode, "(every element)")
+    cu, q2k, tens, ref = _full_case(cfg)
+    m, out = run_gpu(cu, q2k, tens, mode=mode)
+    say("  structures")
+    assert check_structures(m, cu, q2k) == 0
+    check_close("O", to_np(out["O"]), ref["O"])
+    check_lse(to_np(out["LSE"]), ref["LSE"])
+    check_close("dQ", to_np(out["dQ"]), ref["dQ"])
+    dK, dV = to_np(out["dK"]), to_np(out["dV"])
+    check_close("dK", dK, ref["dK"])
+    check_close("dV", dV, ref["dV"])
+    # the most-selected key block (the sink block 0 of the headline workload), alone
+    doc, pos, blk = OR.coords(cu)
+    rp, _ = OR.k2q_csr(q2k, cu)
+    _, _, NB = OR.layout(cu)
+    gb = int(np.argmax(np.diff(rp).reshape(4, NB).sum(0)))
+    cu_ws, _, _ = OR.layout(cu)
+    sel = (cu_ws[doc] + pos) // 128 == gb
+    say("  most-selected block", gb, "(%d task rows per index head):" % int(np.max(
+        (np.diff(rp).reshape(4, NB)[:, gb] + 7) // 8)))
+    check_close("dK[blk]", dK[sel], ref["dK"][sel])
+    check_close("dV[blk]", dV[sel], ref["dV"][sel])
+    _check_common(out, tens)
+
+
+@pytest.mark.parametrize("cfg,mode", [(c, m) for c in (1, 3, 4, LONG) for m in (STORED, RECOMPUTE)]
+                         + [(4, POOL_FP32), (4, POOL_BF16X2)])
 def test_full_size_config(cfg, mode):
     say("config", cfg, "dq mode", mode)
     cu, q2k, tens, qmask, kmask, ref = _case(cfg)
@@ -99,7 +163,4 @@ def test_full_size_config(cfg, mode):
     check_close("dQ", to_np(out["dQ"][qm]), ref["dQ"])
     check_close("dK", to_np(out["dK"][km]), ref["dK"])
     check_close("dV", to_np(out["dV"][km]), ref["dV"])
-    for k in ("O", "dQ", "dK", "dV"):
-        assert torch.isfinite(out[k].float()).all(), k
-    d_ref = (out["O"].float() * tens["dO"].cuda().float()).sum(-1)
-    assert torch.allclose(out["delta"], d_ref, rtol=1e-4, atol=1e-4)
+    _check_common(out, tens)
