@@ -121,7 +121,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--dq-mode", choices=["stored", "recompute", "fp32", "bf16x2"], default="stored")
+    ap.add_argument("--dq-mode", choices=["stored", "recompute", "fp32", "bf16x2", "f16x2"], default="stored")
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -152,7 +152,7 @@ def main():
     q2k_d = torch.from_numpy(q2k).to(dev)
     scale = 1.0 / math.sqrt(128.0)
     mode = {"stored": M.DQ_STORED, "recompute": M.DQ_RECOMPUTE, "fp32": M.DQ_ACCUM_FP32,
-            "bf16x2": M.DQ_ACCUM_BF16X2}[args.dq_mode]
+            "bf16x2": M.DQ_ACCUM_BF16X2, "f16x2": M.DQ_ACCUM_F16X2}[args.dq_mode]
     m = M.MSA(cu, grid=args.grid or None, dq_mode=mode, device=dev)
     O = torch.empty_like(Q)
     LSE = torch.empty((T, 64), dtype=torch.float32, device=dev)

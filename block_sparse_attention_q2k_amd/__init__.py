@@ -19,7 +19,7 @@ from .build import LIB as _LIB_PATH
 NUM_Q_HEADS, NUM_KV_HEADS, NUM_INDEX_HEADS, HEAD_DIM, BLOCK, TOPK = 64, 4, 4, 128, 128, 16
 PLAN_MAX_LIST = 16 * 16
 TILE_QUERIES, FWD_GROUP = 8, 16
-DQ_ACCUM_FP32, DQ_ACCUM_BF16X2, DQ_RECOMPUTE, DQ_STORED = 0, 1, 2, 3
+DQ_ACCUM_FP32, DQ_ACCUM_BF16X2, DQ_RECOMPUTE, DQ_STORED, DQ_ACCUM_F16X2 = 0, 1, 2, 3, 4
 Q2K_OUT_OF_RANGE, Q2K_DUPLICATE = 1, 2
 PLAN_HEADER_WORDS, TASKS_HEADER_WORDS = 16, 64
 

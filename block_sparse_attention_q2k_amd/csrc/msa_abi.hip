@@ -132,6 +132,7 @@ size_t msa_bwd_scratch_bytes(const msa_layout *layout, int dq_accum_mode) {
   switch (dq_accum_mode) {
     case MSA_DQ_ACCUM_FP32: elem = 4; break;
     case MSA_DQ_ACCUM_BF16X2: elem = 2; break;
+    case MSA_DQ_ACCUM_F16X2: elem = 2; break;
     case MSA_DQ_RECOMPUTE: elem = 0; break;
     case MSA_DQ_STORED: elem = 0; break;
     default: return 0;
@@ -231,13 +232,15 @@ int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, cons
   if (rc) return rc;
   if (grid < 1 || grid > MSA_MAX_GRID) return MSA_ERR_GRID;
   if (dq_accum_mode != MSA_DQ_ACCUM_FP32 && dq_accum_mode != MSA_DQ_ACCUM_BF16X2 &&
-      dq_accum_mode != MSA_DQ_RECOMPUTE && dq_accum_mode != MSA_DQ_STORED)
+      dq_accum_mode != MSA_DQ_RECOMPUTE && dq_accum_mode != MSA_DQ_STORED &&
+      dq_accum_mode != MSA_DQ_ACCUM_F16X2)
     return MSA_ERR_MODE;
   if (!scale_ok(scale)) return MSA_ERR_SHAPE;
   if (scratch_bytes < msa_bwd_scratch_bytes(layout, dq_accum_mode)) return MSA_ERR_SCRATCH;
   if ((rc = check_device())) return rc;
   hipStream_t s = (hipStream_t)stream;
-  const bool pool = dq_accum_mode == MSA_DQ_ACCUM_FP32 || dq_accum_mode == MSA_DQ_ACCUM_BF16X2;
+  const bool pool = dq_accum_mode == MSA_DQ_ACCUM_FP32 || dq_accum_mode == MSA_DQ_ACCUM_BF16X2 ||
+                    dq_accum_mode == MSA_DQ_ACCUM_F16X2;
   const bool stored = dq_accum_mode == MSA_DQ_STORED;
   size_t elem = dq_accum_mode == MSA_DQ_ACCUM_FP32 ? 4 : (pool ? 2 : 0);
   size_t dq_bytes = round16((size_t)L.T * MSA_NUM_Q_HEADS * MSA_HEAD_DIM * elem);

@@ -7,7 +7,8 @@
 //   dS = P (dP - delta), dV += P^T dO, dK += scale dS^T Q, dQ += scale dS K.
 // dK/dV accumulate in registers over the consecutive task rows of one bucket and are
 // flushed with fp32 atomics at the end of the bucket segment; dQ is added per task
-// row with atomics into a pool (fp32, or packed bf16 pairs).
+// row with atomics into a pool (fp32, packed bf16 pairs of dims, or packed f16 pairs of
+// heads in a head-pair-interleaved pool).
 //
 // Design (gfx950): a persistent grid; workgroup c walks, for each index head, the task
 // rows [cta[i][c], cta[i][c+1]).  Four waves; wave w owns keys [32w, 32w+32) of the
@@ -41,6 +42,13 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ inline void atomic_add_bf16x2(uint16_t *p, float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
   __builtin_amdgcn_global_atomic_fadd_v2bf16((__attribute__((address_space(1))) bf16x2 *)p, v);
+}
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// Packed f16 pair add (round to nearest even in the conversion): lo, hi = the two heads of
+// a head pair at one dim of the interleaved pool.
+__device__ inline void atomic_add_f16x2(uint32_t *p, float lo, float hi) {
+  f16x2 v = {(_Float16)lo, (_Float16)hi};
+  __builtin_amdgcn_global_atomic_fadd_v2f16((__attribute__((address_space(1))) f16x2 *)p, v);
 }
 
 __global__ void __launch_bounds__(kBwdThreads, 1)
@@ -250,6 +258,17 @@ bwd_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
             for (int nd = 0; nd < 2; ++nd)
 #pragma unroll
               for (int rr = 0; rr < 4; ++rr) atomic_add_f32(pool + rr * kD + 16 * nd, scale * qacc[mt][nd][rr]);
+          } else if (mode == MSA_DQ_ACCUM_F16X2) {
+            // heads 4g + 2hp and 4g + 2hp + 1 of this lane's dim form head pair
+            // 8i + 2g + hp: one packed pair add each, no lane exchange
+            uint32_t *pool = (uint32_t *)dq_pool + ((size_t)tq[q] * (kH / 2) + (kHPI / 2) * i + 2 * g) * kD +
+                             32 * wave + l16;
+#pragma unroll
+            for (int nd = 0; nd < 2; ++nd)
+#pragma unroll
+              for (int hp = 0; hp < 2; ++hp)
+                atomic_add_f16x2(pool + hp * kD + 16 * nd, scale * qacc[mt][nd][2 * hp],
+                                 scale * qacc[mt][nd][2 * hp + 1]);
           } else {
             // pair lanes (l16 even, odd): even lane adds rows 0,1, odd lane rows 2,3
             uint16_t *pool = (uint16_t *)dq_pool + rowbase + 32 * wave + (l16 & ~1);

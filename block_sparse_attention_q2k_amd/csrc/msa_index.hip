@@ -535,7 +535,12 @@ __global__ void preprocess_kernel(const u32x4 *__restrict__ O, const u32x4 *__re
 }
 
 // ------------------------------------------------------------------ finalize
-// Part A (dq_chunks threads): dQ pool -> bf16 dQ, 8 elements per thread.
+// The two f16 halves of a 32-bit word, as fp32.
+__device__ inline float f16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ inline float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// Part A (dq_chunks threads): dQ pool -> bf16 dQ, 8 elements per thread (f16 head-pair
+// pool: 8 dims of both heads of a pair, de-interleaved).
 // Part B: dK/dV pools (fp32 workspace rows) -> bf16 compact rows, 8 elements per thread.
 __global__ void finalize_kernel(const void *__restrict__ dq_pool, int dq_mode, size_t dq_chunks,
                                 const float *__restrict__ dk_pool, const float *__restrict__ dv_pool,
@@ -544,7 +549,23 @@ __global__ void finalize_kernel(const void *__restrict__ dq_pool, int dq_mode, s
                                 u32x4 *__restrict__ dV) {
   size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid < dq_chunks) {
-    if (dq_mode == MSA_DQ_ACCUM_FP32) {
+    if (dq_mode == MSA_DQ_ACCUM_F16X2) {
+      // chunk gid: head pair hp = gid / 16 % 32 of token gid / 512, dims 8 (gid % 16) ..
+      // + 7: 8 words of (even head, odd head) f16 pairs -> 8 bf16 of each head
+      const u32x4 *p = (const u32x4 *)dq_pool + 2 * gid;
+      const u32x4 a = p[0], b = p[1];
+      const uint32_t w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      uint32_t lo[4], hi[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        lo[k] = pack_bf16x2(f16lo(w[2 * k]), f16lo(w[2 * k + 1]));
+        hi[k] = pack_bf16x2(f16hi(w[2 * k]), f16hi(w[2 * k + 1]));
+      }
+      const size_t t = gid / (32 * 16), hp = gid / 16 % 32, c = gid % 16;
+      u32x4 *row = dQ + (t * kH + 2 * hp) * (kD / 8) + c;
+      row[0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      row[kD / 8] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    } else if (dq_mode == MSA_DQ_ACCUM_FP32) {
       const f32x4 *p = (const f32x4 *)dq_pool + 2 * gid;
       f32x4 a = p[0], b = p[1];
       dQ[gid] = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
@@ -701,7 +722,8 @@ hipError_t preprocess(const void *O, const void *dO, int T, float *delta, hipStr
 
 hipError_t finalize(const void *dq_pool, int mode, const float *dk_pool, const float *dv_pool,
                     const LayoutArgs &L, void *dQ, void *dK, void *dV, hipStream_t s) {
-  size_t dq_chunks = dq_pool ? (size_t)L.T * kH * kD / 8 : 0;  // no pool: dQ already final
+  // no pool: dQ already final; f16 pairs: one chunk per (head pair, 8 dims)
+  size_t dq_chunks = dq_pool ? (size_t)L.T * kH * kD / (mode == MSA_DQ_ACCUM_F16X2 ? 16 : 8) : 0;
   size_t kv_chunks = (size_t)L.T * kHKV * kD / 8;
   hipLaunchKernelGGL(finalize_kernel, dim3(blocks_for(dq_chunks + kv_chunks, 256)), dim3(256), 0, s,
                      dq_pool, mode, dq_chunks, dk_pool, dv_pool, L.cu, L.cu_ws, L.ndocs, L.T,

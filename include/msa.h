@@ -70,9 +70,10 @@ enum {
 
 /* How msa_backward forms dQ.  The pages accumulate dQ with 16-bit atomics into a pool
  * (pull-request page, Supported scope; msa_backward_sm100 API page, module summary):
- * modes FP32 and BF16X2 do that (fp32 atomics / packed bf16 pair atomics from the
- * KV-parallel kernel, then a cast).  MSA_DQ_RECOMPUTE instead computes dQ in a
- * query-parallel kernel that recomputes P and dS per selected block and stores dQ
+ * modes FP32, BF16X2 and F16X2 do that (fp32 atomics / packed bf16 pair atomics /
+ * packed f16 head-pair atomics from the KV-parallel kernel, then a cast).
+ * MSA_DQ_RECOMPUTE instead computes dQ in a query-parallel kernel that recomputes P and
+ * dS per selected block and stores dQ
  * directly (no pool, no atomics); on gfx950 global atomic throughput, not the matrix
  * cores, bounds the pooled modes.  MSA_DQ_STORED has the KV-parallel kernel, which forms
  * every dS value anyway, store each (query, index head, member slot) dS tile (bf16,
@@ -80,7 +81,18 @@ enum {
  * recomputation and no atomics, at 4 KiB x 16 x 4 = 256 KiB of scratch per token; the
  * fastest, and the default of the Python binding.  Modes differ in rounding only (dS is
  * rounded to bf16 before its products in all of them). */
-enum { MSA_DQ_ACCUM_FP32 = 0, MSA_DQ_ACCUM_BF16X2 = 1, MSA_DQ_RECOMPUTE = 2, MSA_DQ_STORED = 3 };
+enum {
+  MSA_DQ_ACCUM_FP32 = 0,
+  MSA_DQ_ACCUM_BF16X2 = 1,
+  MSA_DQ_RECOMPUTE = 2,
+  MSA_DQ_STORED = 3,
+  /* Packed-f16 pair atomics into a head-pair-interleaved pool, the pages' default
+   * accumulator (pull-request page, Supported scope: FP16 dQ by default;
+   * msa_backward_sm100 API page, module summary: head-pair-interleaved pool, packed f16
+   * pair reduction).  Pool element (t, h, d) is the f16 at half (h % 2) of 32-bit word
+   * (t * 32 + h / 2) * 128 + d; the finalize step de-interleaves it to bf16 dQ. */
+  MSA_DQ_ACCUM_F16X2 = 4
+};
 
 #define MSA_MAX_GRID 4096
 

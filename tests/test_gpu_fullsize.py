@@ -11,7 +11,7 @@ launch configuration the benchmark times (default grid = one workgroup per CU).
   (the largest buckets, whose rows are split over the most workgroups) plus two random
   ones, whose selecting queries the oracle enumerates in full.  The 4 x 16384-token
   batch of short documents (Zipf-skewed picks, the workload that concentrates atomic
-  traffic) also runs the two pooled dQ modes.
+  traffic) also runs the three pooled dQ modes.
 * At every row: finiteness, and delta = rowsum(dO * O)."""
 import functools
 
@@ -25,8 +25,9 @@ from _gpu_util import SCALE, check_close, check_lse, check_structures, run_gpu, 
 
 pytestmark = pytest.mark.gpu
 
-# dQ modes of the library: 0 fp32 pool, 1 packed-bf16 pool, 2 recompute, 3 stored dS
-STORED, RECOMPUTE, POOL_FP32, POOL_BF16X2 = 3, 2, 0, 1
+# dQ modes of the library: 0 fp32 pool, 1 packed-bf16 pool, 2 recompute, 3 stored dS,
+# 4 packed-f16 head-pair pool
+STORED, RECOMPUTE, POOL_FP32, POOL_BF16X2, POOL_F16X2 = 3, 2, 0, 1, 4
 
 
 def _sample_rows(cu, rng, n=40):
@@ -120,7 +121,7 @@ def _check_common(out, tens):
     assert torch.allclose(out["delta"], d_ref, rtol=1e-4, atol=1e-4)
 
 
-@pytest.mark.parametrize("mode", [STORED, RECOMPUTE, POOL_FP32, POOL_BF16X2])
+@pytest.mark.parametrize("mode", [STORED, RECOMPUTE, POOL_FP32, POOL_BF16X2, POOL_F16X2])
 @pytest.mark.parametrize("cfg", [0, 2])
 def test_full_size_every_element(cfg, mode):
     say("config", cfg, "dq mode", mode, "(every element)")
@@ -149,7 +150,7 @@ def test_full_size_every_element(cfg, mode):
 
 
 @pytest.mark.parametrize("cfg,mode", [(c, m) for c in (1, 3, 4, LONG) for m in (STORED, RECOMPUTE)]
-                         + [(4, POOL_FP32), (4, POOL_BF16X2)])
+                         + [(4, POOL_FP32), (4, POOL_BF16X2), (4, POOL_F16X2)])
 def test_full_size_config(cfg, mode):
     say("config", cfg, "dq mode", mode)
     cu, q2k, tens, qmask, kmask, ref = _case(cfg)

@@ -76,7 +76,7 @@ def test_forward_parity_small(name):
     check_lse(to_np(out["LSE"]), LSE)
 
 
-@pytest.mark.parametrize("mode", [3, 2, 0, 1])
+@pytest.mark.parametrize("mode", [3, 2, 0, 1, 4])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_backward_parity_small(name, mode):
     say("case", name, "dq mode", mode)
