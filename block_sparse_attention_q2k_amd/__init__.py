@@ -41,7 +41,7 @@ EXPORTS = ["msa_layout_host", "msa_csr_scratch_bytes", "msa_csr_cols_capacity", 
            "msa_tasks_bytes", "msa_bwd_scratch_bytes", "msa_default_grid", "msa_align_kv",
            "msa_build_k2q_csr", "msa_plan", "msa_forward", "msa_backward_preprocess",
            "msa_tasks_meta_offset", "msa_build_tasks", "msa_backward", "msa_status_string",
-           "msa_set_timing_events"]
+           "msa_set_timing_events", "msa_build_k2q_csr_noalloc"]
 
 
 def lib():
@@ -68,6 +68,7 @@ def lib():
             "msa_default_grid": (I, []),
             "msa_align_kv": (I, [P, P, LP, P, P, P, P, P]),
             "msa_build_k2q_csr": (I, [P, LP, P, P, P, P, Z, P]),
+            "msa_build_k2q_csr_noalloc": (I, [P, LP, P, P, P, P]),
             "msa_plan": (I, [LP, P, P, Z, P]),
             "msa_forward": (I, [P, P, P, P, LP, P, F, P, P, P]),
             "msa_backward_preprocess": (I, [P, P, I, P, P]),
@@ -213,6 +214,20 @@ def msa_build_k2q_csr(q2k, layout, row_ptr, cols, status, scratch, stream=None):
     _check("msa_build_k2q_csr", lib().msa_build_k2q_csr(
         _ptr(q2k), layout.ref(), _ptr(row_ptr), _ptr(cols), _ptr(status), _ptr(scratch),
         scratch.numel() * scratch.element_size(), _stream(stream)))
+
+
+def msa_build_k2q_csr_noalloc(q2k, layout, row_ptr, cols, status, stream=None):
+    """msa_build_k2q_csr without a scratch argument: the library's own device array holds
+    the counters (for callers that cannot allocate; calls on one GPU must not overlap)."""
+    _, _, i32, _ = _dt()
+    fn = "msa_build_k2q_csr_noalloc"
+    _need_q2k(fn, q2k, layout)
+    _need(fn, "row_ptr", row_ptr, i32, min_numel=NUM_INDEX_HEADS * layout.NB + 1)
+    _need(fn, "cols", cols, i32, min_numel=msa_csr_cols_capacity(layout))
+    _need(fn, "status", status, i32, min_numel=1)
+    _gpu(fn, q2k=q2k, row_ptr=row_ptr, cols=cols, status=status)
+    _check(fn, lib().msa_build_k2q_csr_noalloc(_ptr(q2k), layout.ref(), _ptr(row_ptr), _ptr(cols),
+                                               _ptr(status), _stream(stream)))
 
 
 def msa_plan(layout, q2k, plan, stream=None):

@@ -3,11 +3,19 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "msa_device.h"
 #include "msa_launch.h"
 
 using namespace msa;
+
+// Counters of msa_build_k2q_csr_noalloc (one int32 per CSR row, 4 index heads x the
+// largest block count a layout may have, 2 MiB): a device array of the library, so that
+// the call allocates nothing.  Each GPU holds its own copy until the process ends; host
+// code uses only the per-device address from hipGetSymbolAddress, never this name.
+constexpr size_t kNoAllocCsrWords = (size_t)MSA_NUM_INDEX_HEADS * ((size_t)1 << 24) / MSA_BLOCK;
+static __device__ __align__(256) int32_t scratch[kNoAllocCsrWords];
 
 namespace {
 
@@ -68,6 +76,24 @@ size_t round16(size_t b) { return (b + 15) / 16 * 16; }
 // spare tile that the KV-parallel kernel writes for the padding queries of a task row.
 size_t ds_store_bytes(const LayoutArgs &L) {
   return ((size_t)L.T * MSA_NUM_INDEX_HEADS * MSA_TOPK + 1) * 16 * MSA_BLOCK * 2;
+}
+
+// Device address of `scratch` per device, looked up once (with that device current) on
+// the first msa_build_k2q_csr_noalloc call there.
+std::mutex g_scratch_mu;
+int32_t *g_scratch_ptr[64] = {};
+
+int noalloc_scratch(int32_t **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MSA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MSA_ERR_DEVICE;
+    g_scratch_ptr[dev] = (int32_t *)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
 }
 
 thread_local hipEvent_t t_events[MSA_TIMING_EVENTS] = {};
@@ -172,6 +198,19 @@ int msa_build_k2q_csr(const int32_t *q2k, const msa_layout *layout, int32_t *row
   if ((rc = check_device())) return rc;
   return launch_rc(host::build_csr(q2k, L, row_ptr, cols, status, (int32_t *)scratch,
                                    (hipStream_t)stream));
+}
+
+int msa_build_k2q_csr_noalloc(const int32_t *q2k, const msa_layout *layout, int32_t *row_ptr,
+                              int32_t *cols, int32_t *status, void *stream) {
+  LayoutArgs L;
+  int rc = check_layout(layout, &L);
+  if (!rc) rc = check_ptrs({q2k, row_ptr, cols, status});
+  if (rc) return rc;
+  if ((size_t)MSA_NUM_INDEX_HEADS * L.NB > kNoAllocCsrWords) return MSA_ERR_SCRATCH;
+  if ((rc = check_device())) return rc;
+  int32_t *counters = nullptr;
+  if ((rc = noalloc_scratch(&counters))) return rc;
+  return launch_rc(host::build_csr(q2k, L, row_ptr, cols, status, counters, (hipStream_t)stream));
 }
 
 int msa_plan(const msa_layout *layout, const int32_t *q2k, void *plan, size_t plan_bytes,

@@ -169,6 +169,18 @@ int msa_build_k2q_csr(const int32_t *q2k, const msa_layout *layout, int32_t *row
                       int32_t *cols, int32_t *status, void *scratch, size_t scratch_bytes,
                       void *stream);
 
+/* The same CSR inversion for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): no scratch
+ * argument; the per-row counters live in a 2 MiB device array of the library (each GPU
+ * it runs on holds its own copy until the process ends), cleared by a kernel at the start
+ * of every call.  The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).  Layouts with more than 4 * (2^24 / 128) CSR rows return MSA_ERR_SCRATCH (no
+ * layout msa_layout_host accepts has that many).  Calls on one GPU share that array, so
+ * calls that overlap on one GPU (other streams, other host threads) race; serialize them.
+ * Same arguments, outputs and errors as msa_build_k2q_csr otherwise. */
+int msa_build_k2q_csr_noalloc(const int32_t *q2k, const msa_layout *layout, int32_t *row_ptr,
+                              int32_t *cols, int32_t *status, void *stream);
+
 /* ---------------------------------------------------------------------------------
  * Forward plan (the forward schedule; bindings page: fmha_sm100_plan).  Cuts every
  * document into groups of MSA_FWD_GROUP consecutive queries; each (index head, group)
