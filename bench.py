@@ -48,6 +48,78 @@ def member_slots(q2k, cu):
     return int((ok & first).sum())
 
 
+def visible_keys(q2k, cu):
+    """Keys each member slot actually lets its query see (causal): 128 for a block before
+    the query's own, pos(t) % 128 + 1 for its own block.  Summed over the slots; the
+    whole-block count charges 128 for every slot."""
+    T = int(cu[-1])
+    t = np.arange(T)
+    doc = np.searchsorted(cu, t, side="right") - 1
+    pos = t - cu[doc]
+    blk = pos // 128
+    ok = (q2k >= 0) & (q2k <= blk[None, :, None])
+    first = np.ones_like(ok)
+    for j in range(1, q2k.shape[2]):
+        first[:, :, j] = ~np.any(q2k[:, :, :j] == q2k[:, :, j:j + 1], axis=2)
+    keys = np.where(q2k == blk[None, :, None], (pos % 128 + 1)[None, :, None], 128)
+    return int((keys * (ok & first)).sum())
+
+
+def sweep(args, M, WL, torch):
+    """Single 16-top-k document at T = 4k, 8k, 16k, 32k tokens (the sequence lengths of
+    the pages' operator benchmark), selection as in workload 2 (diagonal + block 0 + 14
+    uniform blocks): one JSON line per T with forward / backward medians, effective
+    TFLOP/s and the peak device memory of one forward + backward (inputs, outputs and
+    every library buffer, the stored dS tiles included), and of the same call sequence in
+    the recompute dQ mode, which needs no dS tiles."""
+    dev = "cuda:0"
+    scale = 1.0 / math.sqrt(128.0)
+    for T in (4096, 8192, 16384, 32768):
+        cu, q2k = WL.make_custom([T], "sink", 2)
+        slots = member_slots(q2k, cu)
+        fwd_flops = 4.0 * 128 * 128 * 16 * slots
+        bwd_flops = 2.5 * fwd_flops
+        peak = {}
+        for name, mode in (("recompute", M.DQ_RECOMPUTE), ("stored", M.DQ_STORED)):
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            torch.cuda.reset_peak_memory_stats()
+            base = torch.cuda.memory_allocated()
+            tens = WL.make_tensors(T, 3000 + T, device=dev)
+            Q, K, V, dO = tens["Q"], tens["K"], tens["V"], tens["dO"]
+            q2k_d = torch.from_numpy(q2k).to(dev)
+            m = M.MSA(cu, dq_mode=mode, device=dev)
+            O, LSE = m.forward(Q, K, V, q2k_d, scale)
+            dQ, dK, dV = m.backward(Q, dO, O, LSE, scale)
+            torch.cuda.synchronize()
+            peak[name] = (torch.cuda.max_memory_allocated() - base) / 1e9
+            if name == "recompute":
+                del m, O, LSE, dQ, dK, dV, tens, Q, K, V, dO, q2k_d
+        fwd_ms, bwd_ms = [], []
+        for k in range(args.warmup + args.steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record()
+            m.forward(Q, K, V, q2k_d, scale, O=O, LSE=LSE)
+            ev[1].record()
+            m.backward(Q, dO, O, LSE, scale, dQ=dQ, dK=dK, dV=dV)
+            ev[2].record()
+            torch.cuda.synchronize()
+            if k >= args.warmup:
+                fwd_ms.append(ev[0].elapsed_time(ev[1]))
+                bwd_ms.append(ev[1].elapsed_time(ev[2]))
+        f, b = float(np.median(fwd_ms)), float(np.median(bwd_ms))
+        print(json.dumps({
+            "sweep": "single document, top-16 (diagonal + block 0 + 14 uniform), 64 q / 4 kv heads",
+            "tokens": T, "member_slots": slots, "dq_accum": "stored",
+            "fwd_ms_median": round(f, 4), "bwd_ms_median": round(b, 4), "ms_per_layer": round(f + b, 4),
+            "fwd_tflops": round(fwd_flops / f / 1e9, 2), "bwd_tflops": round(bwd_flops / b / 1e9, 2),
+            "tflops": round((fwd_flops + bwd_flops) / (f + b) / 1e9, 2),
+            "frac_mfma_peak": round((fwd_flops + bwd_flops) / (f + b) / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "peak_gb": round(peak["stored"], 3), "peak_gb_recompute_mode": round(peak["recompute"], 3),
+            "steps": args.steps, "warmup": args.warmup}), flush=True)
+        del m, O, LSE, dQ, dK, dV, tens, Q, K, V, dO, q2k_d
+
+
 def cpu_baseline(cfg, budget_tokens):
     """The fp64 oracle on a bounded sample: the first `budget_tokens` queries of the
     workload's first document with their own selections.  A prefix of a causal
@@ -125,6 +197,8 @@ def main():
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="single-document sequence sweep (T = 4k..32k) with peak memory, one line per T")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB buffer a few times (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -145,6 +219,9 @@ def main():
     M.lib()
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.sweep:
+        sweep(args, M, WL, torch)
+        return
     cu, q2k = WL.make_structure(args.config)
     T = int(cu[-1])
     tens = WL.make_tensors(T, 1000 + args.config, device=dev)
@@ -163,6 +240,7 @@ def main():
     slots = member_slots(q2k, cu)
     fwd_flops = 4.0 * 128 * 128 * 16 * slots
     bwd_flops = 2.5 * fwd_flops
+    causal_fraction = visible_keys(q2k, cu) / (128.0 * slots)  # keys a query can see / charged keys
 
     def step(ev=None):
         if ev:
@@ -248,6 +326,11 @@ def main():
         "fwd_frac_mfma_peak": round(fwd_flops / (np.median(fwd_ms) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "bwd_frac_mfma_peak": round(bwd_flops / (np.median(bwd_ms) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "q2k_status": status,
+        "flop_convention": "every member block counts all 128 keys for its 16 heads (4*128 flop per "
+                           "(row, key) forward, 10*128 backward); keys a query can causally see are "
+                           "causal_fraction of those",
+        "causal_fraction": round(causal_fraction, 4),
+        "causal_tflops": round(value * causal_fraction, 3),
         "roofline": {"kernel": "main backward: " + " + ".join(k["kernel"] for k in kernels[1:]),
                      "bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -70,7 +70,7 @@ def lib():
             "msa_build_k2q_csr": (I, [P, LP, P, P, P, P, Z, P]),
             "msa_build_k2q_csr_noalloc": (I, [P, LP, P, P, P, P]),
             "msa_plan": (I, [LP, P, P, Z, P]),
-            "msa_forward": (I, [P, P, P, P, LP, P, F, P, P, P]),
+            "msa_forward": (I, [P, P, P, LP, P, F, P, P, P]),
             "msa_backward_preprocess": (I, [P, P, I, P, P]),
             "msa_tasks_meta_offset": (Z, [I]),
             "msa_build_tasks": (I, [LP, P, P, P, I, P, Z, P]),
@@ -238,7 +238,7 @@ def msa_plan(layout, q2k, plan, stream=None):
                                       plan.numel() * plan.element_size(), _stream(stream)))
 
 
-def msa_forward(Q, Kw, Vt, q2k, layout, plan, scale, O, LSE, stream=None):
+def msa_forward(Q, Kw, Vt, layout, plan, scale, O, LSE, stream=None):
     bf, f32, _, _ = _dt()
     fn = "msa_forward"
     for n, t in (("Q", Q), ("O", O)):
@@ -246,12 +246,10 @@ def msa_forward(Q, Kw, Vt, q2k, layout, plan, scale, O, LSE, stream=None):
     for n, t in (("Kw", Kw), ("Vt", Vt)):
         _need(fn, n, t, bf, min_numel=layout.W * NUM_KV_HEADS * HEAD_DIM)
     _need(fn, "LSE", LSE, f32, (layout.T, NUM_Q_HEADS))
-    _need_q2k(fn, q2k, layout)
     _need(fn, "plan", plan, None, min_numel=msa_plan_bytes(layout) // plan.element_size())
-    _gpu(fn, Q=Q, Kw=Kw, Vt=Vt, q2k=q2k, plan=plan, O=O, LSE=LSE)
-    _check("msa_forward", lib().msa_forward(_ptr(Q), _ptr(Kw), _ptr(Vt), _ptr(q2k), layout.ref(),
-                                            _ptr(plan), float(scale), _ptr(O), _ptr(LSE),
-                                            _stream(stream)))
+    _gpu(fn, Q=Q, Kw=Kw, Vt=Vt, plan=plan, O=O, LSE=LSE)
+    _check("msa_forward", lib().msa_forward(_ptr(Q), _ptr(Kw), _ptr(Vt), layout.ref(), _ptr(plan),
+                                            float(scale), _ptr(O), _ptr(LSE), _stream(stream)))
 
 
 def msa_backward_preprocess(O, dO, num_tokens, delta, stream=None):
@@ -356,7 +354,7 @@ class MSA:
         msa_build_k2q_csr(q2k, L, self.row_ptr, self.cols, self.status, self.csr_scratch, stream)
         msa_plan(L, q2k, self.plan, stream)
         msa_align_kv(K, V, L, self.Kw, self.Vw, self.Kt, self.Vt, stream)
-        msa_forward(Q, self.Kw, self.Vt, q2k, L, self.plan, scale, O, LSE, stream)
+        msa_forward(Q, self.Kw, self.Vt, L, self.plan, scale, O, LSE, stream)
         self.q2k = q2k
         return O, LSE
 

@@ -224,17 +224,16 @@ int msa_plan(const msa_layout *layout, const int32_t *q2k, void *plan, size_t pl
   return launch_rc(host::build_plan(L, q2k, plan, (hipStream_t)stream));
 }
 
-int msa_forward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vt, const int32_t *q2k,
-                const msa_layout *layout, const void *plan, float scale, msa_bf16 *O,
-                float *LSE, void *stream) {
+int msa_forward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vt, const msa_layout *layout,
+                const void *plan, float scale, msa_bf16 *O, float *LSE, void *stream) {
   LayoutArgs L;
   int rc = check_layout(layout, &L);
-  if (!rc) rc = check_ptrs({Q, Kw, Vt, q2k, plan, O, LSE});
+  if (!rc) rc = check_ptrs({Q, Kw, Vt, plan, O, LSE});
   if (rc) return rc;
   if (!scale_ok(scale)) return MSA_ERR_SHAPE;
   if ((rc = check_device())) return rc;
   hipError_t e = mark(0, (hipStream_t)stream);
-  if (e == hipSuccess) e = host::forward(Q, Kw, Vt, q2k, L, plan, scale, O, LSE, (hipStream_t)stream);
+  if (e == hipSuccess) e = host::forward(Q, Kw, Vt, L, plan, scale, O, LSE, (hipStream_t)stream);
   if (e == hipSuccess) e = mark(1, (hipStream_t)stream);
   return launch_rc(e);
 }

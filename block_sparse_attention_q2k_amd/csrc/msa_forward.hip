@@ -439,10 +439,8 @@ fwd_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
 }
 
 namespace host {
-hipError_t forward(const void *Q, const void *Kw, const void *Vt, const int32_t *q2k,
-                   const LayoutArgs &L, const void *plan, float scale, void *O, float *LSE,
-                   hipStream_t s) {
-  (void)q2k;  // the walk lists of the plan carry the selection
+hipError_t forward(const void *Q, const void *Kw, const void *Vt, const LayoutArgs &L, const void *plan,
+                   float scale, void *O, float *LSE, hipStream_t s) {
   PlanView v = plan_view(L, const_cast<void *>(plan));
   const unsigned items = (unsigned)(kHI * plan_gmax(L));
   hipLaunchKernelGGL(fwd_kernel<false>, dim3(items), dim3(kWalkThreads), 0, s, (const uint16_t *)Q,

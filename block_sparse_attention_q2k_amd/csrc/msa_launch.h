@@ -39,8 +39,7 @@ hipError_t build_tasks(const LayoutArgs &L, const int32_t *row_ptr, const int32_
 hipError_t preprocess(const void *O, const void *dO, int T, float *delta, hipStream_t s);
 hipError_t finalize(const void *dq_pool, int mode, const float *dk_pool, const float *dv_pool,
                     const LayoutArgs &L, void *dQ, void *dK, void *dV, hipStream_t s);
-hipError_t forward(const void *Q, const void *Kw, const void *Vt, const int32_t *q2k,
-                   const LayoutArgs &L, const void *plan, float scale, void *O, float *LSE,
+hipError_t forward(const void *Q, const void *Kw, const void *Vt, const LayoutArgs &L, const void *plan, float scale, void *O, float *LSE,
                    hipStream_t s);
 hipError_t backward_main(const void *Q, const void *Kw, const void *Vw, const void *dO,
                          const float *LSE, const float *delta, const void *tasks,

@@ -200,15 +200,14 @@ int msa_plan(const msa_layout *layout, const int32_t *q2k, void *plan, size_t pl
 
 /* ---------------------------------------------------------------------------------
  * Forward (pull-request page, Design: Q[T,64,128], K/V, q2k -> O[T,64,128] + LSE).
- *   Q: bf16 [T, 64, 128].  Kw and Vt from msa_align_kv.  plan from msa_plan.  q2k as
- *   above.  scale: the softmax scale applied to Q K^T, finite and > 0 (else
- *   MSA_ERR_SHAPE).
+ *   Q: bf16 [T, 64, 128].  Kw and Vt from msa_align_kv.  plan from msa_plan (its walk
+ *   lists carry the selection).  scale: the softmax scale applied to Q K^T, finite and
+ *   > 0 (else MSA_ERR_SHAPE).
  *   O: bf16 [T, 64, 128].  LSE: fp32 [T, 64], natural log of the sum of exp(scores),
  *   scores including `scale`; -inf (and O = 0) for a row with no keys.
  * --------------------------------------------------------------------------------- */
-int msa_forward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vt, const int32_t *q2k,
-                const msa_layout *layout, const void *plan, float scale, msa_bf16 *O,
-                float *LSE, void *stream);
+int msa_forward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vt, const msa_layout *layout,
+                const void *plan, float scale, msa_bf16 *O, float *LSE, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * Backward preprocessing (pull-request page, Custom kernel: delta preprocessing).
@@ -233,7 +232,8 @@ int msa_backward_preprocess(const msa_bf16 *O, const msa_bf16 *dO, int32_t num_t
  *     first row of its bucket, bit1 = last);
  *   qrows, qpos, qtile: Rmax x 8 int32 each (query ids; document-local positions;
  *     stored-dS tile index (t * 4 + i) * 16 + j with j the first slot of q2k[i][t]
- *     listing the bucket's block; -1 pad).  q2k is the device q2k the CSR was built from.
+ *     listing the bucket's block; -1 pad).  q2k must be the device q2k the CSR was built
+ *     from (the same array contents; a different q2k gives wrong tile indices, unchecked).
  * Rows inside one bucket appear in ascending k; their query sets follow the CSR order.
  * --------------------------------------------------------------------------------- */
 size_t msa_tasks_meta_offset(int32_t grid);
@@ -243,8 +243,10 @@ int msa_build_tasks(const msa_layout *layout, const int32_t *row_ptr, const int3
 /* ---------------------------------------------------------------------------------
  * Backward (msa_backward_sm100 API page, run_backward and module summary):
  *   Q, dO: bf16 [T, 64, 128]; Kw, Vw, Kt from msa_align_kv; LSE fp32 [T, 64] from
- *   msa_forward; delta from msa_backward_preprocess; q2k and plan as given to the
- *   forward; tasks from msa_build_tasks and `grid` the value it was built with (the
+ *   msa_forward; delta from msa_backward_preprocess; q2k and plan those the CSR and
+ *   the forward were built from (the stored-dS and recompute modes look blocks up in
+ *   them; a different q2k is not detected and gives wrong dQ); tasks from
+ *   msa_build_tasks and `grid` the value it was built with (the
  *   KV-parallel launch uses that many workgroups).  scale: the forward's softmax scale
  *   (finite and > 0, else MSA_ERR_SHAPE).  Writes dQ bf16 [T, 64, 128] and
  *   dK, dV bf16 [T, 4, 128] in compact token order.  scratch >=
@@ -264,8 +266,8 @@ int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, cons
  * turns the hook off).  While set, calls from this host thread record, on the call's
  * stream: events[0] / [1] right before / after the forward kernel launches of
  * msa_forward; events[2] / [3] around the KV-parallel backward kernel of msa_backward
- * (dK/dV, plus the dQ atomics of the pooled modes); events[4] / [5] around its dQ kernel
- * (MSA_DQ_RECOMPUTE only).  The array is copied; the caller keeps the events alive while
+ * (dK/dV, plus the dQ atomics of the pooled modes); events[4] / [5] around its
+ * query-parallel dQ kernel (MSA_DQ_RECOMPUTE and MSA_DQ_STORED).  The array is copied; the caller keeps the events alive while
  * the hook is set.  Lets a caller time each kernel alone. */
 #define MSA_TIMING_EVENTS 6
 void msa_set_timing_events(void *const *events);

@@ -86,7 +86,7 @@ def test_argument_errors_return_before_device_use(M):
     assert lib.msa_align_kv(a, a, L.ref(), a, mis, a, a, None) == E["ALIGN"]
     assert lib.msa_build_k2q_csr(a, L.ref(), a, a, a, a, 1, None) == E["SCRATCH"]
     assert lib.msa_plan(L.ref(), a, a, 16, None) == E["SCRATCH"]
-    assert lib.msa_forward(a, a, a, a, L.ref(), a, ctypes.c_float(-1.0), a, a, None) == E["SHAPE"]
+    assert lib.msa_forward(a, a, a, L.ref(), a, ctypes.c_float(-1.0), a, a, None) == E["SHAPE"]
     assert lib.msa_backward_preprocess(a, a, 0, a, None) == E["SHAPE"]
     assert lib.msa_build_tasks(L.ref(), a, a, a, 0, a, 1 << 30, None) == E["GRID"]
     bw = lambda grid, mode, nbytes: lib.msa_backward(a, a, a, a, a, a, a, a, a, a, grid, L.ref(),
@@ -97,7 +97,7 @@ def test_argument_errors_return_before_device_use(M):
     assert bw(256, 2, 16) == E["SCRATCH"]
     # the softmax scale must be finite and positive (checked before the device)
     for sc in (0.0, -0.5, float("nan"), float("inf")):
-        assert lib.msa_forward(a, a, a, a, L.ref(), a, ctypes.c_float(sc), a, a, None) == E["SHAPE"], sc
+        assert lib.msa_forward(a, a, a, L.ref(), a, ctypes.c_float(sc), a, a, None) == E["SHAPE"], sc
         assert lib.msa_backward(a, a, a, a, a, a, a, a, a, a, 256, L.ref(), ctypes.c_float(sc), 2, a, a, a, a,
                                 1 << 40, None) == E["SHAPE"], sc
     bad = FakeLayout(M, T=1000, W=1000)
@@ -117,14 +117,14 @@ def test_binding_refuses_tensors_the_kernels_would_overrun(M):
     q2k = torch.full((4, T, 16), -1, dtype=i32)
     plan = torch.zeros(M.msa_plan_bytes(L), dtype=torch.uint8)
     LSE = torch.zeros((T, 64), dtype=f32)
-    call = lambda **kw: M.msa_forward(**{**dict(Q=Q, Kw=Kw, Vt=Kw, q2k=q2k, layout=L, plan=plan, scale=0.1,
+    call = lambda **kw: M.msa_forward(**{**dict(Q=Q, Kw=Kw, Vt=Kw, layout=L, plan=plan, scale=0.1,
                                                 O=Q, LSE=LSE), **kw})
     with pytest.raises(ValueError, match="dtype"):
         call(Q=Q.float())
     with pytest.raises(ValueError, match="shape"):
         call(O=torch.zeros((T - 1, 64, 128), dtype=bf))
     with pytest.raises(ValueError, match="shape"):
-        call(q2k=torch.full((4, T, 8), -1, dtype=i32))
+        call(LSE=torch.zeros((T, 32), dtype=f32))
     with pytest.raises(ValueError, match="at least"):
         call(Kw=torch.zeros((W - 128, 4, 128), dtype=bf))
     with pytest.raises(ValueError, match="contiguous"):
