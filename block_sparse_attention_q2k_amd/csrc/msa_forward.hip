@@ -141,7 +141,11 @@ __device__ __forceinline__ void fwd_pair_load(const FwdCtx &x, FwdPair &pr, uint
 // S phase of one step (units mr): pairs in unit order at slots 0, 2, 4, ...  Once a
 // pair's MFMAs are issued (they have read their operands), the same registers are
 // refilled with the next pair's Q rows, which then arrive behind the MFMAs and the
-// current pair's softmax.
+// current pair's softmax.  MASKED: the step's block is the diagonal block of some unit;
+// otherwise no key needs the causal mask and the pair loop carries no mask code (whose
+// divergent select would move every score tile out of the accumulation registers and
+// back).
+template <bool MASKED>
 __device__ __forceinline__ void fwd_scores(const FwdCtx &x, const bf16x8 (&k)[8], uint32_t mr, int b,
                                            uint32_t dmask) {
   FwdPair pr;
@@ -154,7 +158,7 @@ __device__ __forceinline__ void fwd_scores(const FwdCtx &x, const bf16x8 (&k)[8]
     f32x16 st = tile32(k, pr.q);
     const bool more = ms != 0;
     if (more) fwd_pair_load(x, pr, ms);
-    fwd_tile_mask(x, st, u0, u1, b, diag);
+    if (MASKED) fwd_tile_mask(x, st, u0, u1, b, diag);
     fwd_tile_p(x, st, s0, mn);
     if (!more) break;
   }
@@ -315,7 +319,10 @@ __device__ __forceinline__ void fwd_step(const FwdCtx &x, int a, FwdPos &q, cons
   seen |= m;
   // ---- S phase: the step's units in pairs, this wave's keys (one slot per unit)
   fwd_load_k_half<1>(x, kn, q.bn);
-  fwd_scores(x, kc, m, b, dmask);
+  if (dmask & m)
+    fwd_scores<true>(x, kc, m, b, dmask);
+  else
+    fwd_scores<false>(x, kc, m, b, dmask);
   lds_barrier();
   fwd_load_v_half<0>(x, vn, q.bn);
   WAIT_VMCNT(12);  // this step's V^T slices
