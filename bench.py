@@ -149,20 +149,22 @@ def cpu_baseline(cfg, budget_tokens):
 
 # HBM bytes per launch of the main backward kernels at the headline workload (config 2,
 # dQ from stored dS tiles), from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by the same counters'
-# reading for a plain copy of known size; valid only for the kernel sources they were
-# taken on (sha256 over the files below).
-TRAFFIC_SOURCES = ["msa_backward_kv.hip", "msa_backward_dq.hip", "msa_backward_dqs.hip", "msa_walk.h", "msa_device.h",
-                   "msa_launch.h"]
+# reading for a plain copy of known size; valid only for the build they were taken on:
+# sha256 over every library source the backward launches depend on (the forward's own
+# file excepted) and the build script with its compiler flags.
+TRAFFIC_SOURCES = ["msa_abi.hip", "msa_backward.hip", "msa_backward_kv.hip", "msa_backward_dq.hip",
+                   "msa_backward_dqs.hip", "msa_index.hip", "msa_walk.h", "msa_device.h", "msa_launch.h",
+                   "../build.py"]
 TRAFFIC_RECORD = {"config": 2, "dq_mode": "stored",
-                  "sha256": "656c53f63e272e448142cb37e957d97dc11fa50b1f4c1a419f453999d9609ffc",
-                  "bytes": 17025781560}  # read 12.514 GB + written 4.512 GB
+                  "sha256": "38e6e1dfbcc960038742884ef02822599d79556a0fca34ce676d55a428b6d81e",
+                  "bytes": 17028731056}  # read 12.510 GB + written 4.518 GB
 
 
 def sources_digest():
     import hashlib
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, "block_sparse_attention_q2k_amd", "csrc", f), "rb") as fh:
+        with open(os.path.normpath(os.path.join(ROOT, "block_sparse_attention_q2k_amd", "csrc", f)), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 

@@ -148,3 +148,15 @@ def test_product_path_has_no_oracle_dependency():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in txt.lower(), f
+
+
+def test_bench_traffic_digest_covers_existing_sources():
+    """bench.py reports recorded HBM traffic only for the build it was measured on; every
+    file of that digest must exist (a renamed source would otherwise break the bench)."""
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    for f in bench.TRAFFIC_SOURCES:
+        assert os.path.exists(os.path.normpath(os.path.join(root, "block_sparse_attention_q2k_amd", "csrc", f))), f
+    assert len(bench.sources_digest()) == 64
