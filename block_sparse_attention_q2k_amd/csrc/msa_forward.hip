@@ -41,6 +41,7 @@ namespace msa {
 
 constexpr int kFwdSlots = kFwdGroup;  // P slots: one per unit of the item
 static_assert(kFwdGroup <= 32, "unit masks are 32-bit");
+static_assert((kFwdSlots & (kFwdSlots - 1)) == 0, "the P slots form a ring indexed modulo their count");
 
 struct FwdCtx {
   WalkLane w;
@@ -50,7 +51,11 @@ struct FwdCtx {
   float c;  // scale * log2(e)
   const char *sQ;
   char *sP;
+  int sbase;  // ring position of the step's first P slot
   float *sM, *sX;  // references [unit][head]; exchange area [wave][unit][head]
+  const char *qrow;   // this lane's Q row of unit 0: sQ + l16 * kUnitRow + 16 hi
+  const float *mrow;  // this lane's reference of unit 0: sM + l16
+  bool lo;            // lane l32 < 16: the first unit of a pair
 };
 
 // Workspace block index (KV head, block) of the item's block b.
@@ -106,8 +111,8 @@ __device__ __forceinline__ float fwd_tile_max(const f32x16 &st) {
   return fmaxf(mx, __shfl_xor(mx, 32));
 }
 
-// P = 2^(c s - mn) of the tile, as bf16, to the slots of its units (slot s0 + column
-// half).  `two`: the second half holds a unit (otherwise its P lands in an unused
+// P = 2^(c s - mn) of the tile, as bf16, to the slots of its units (the step's slot s0 +
+// column half, counted on the ring from the step's first slot).  `two`: the second half holds a unit (otherwise its P lands in an unused
 // slot); mn: this lane's column reference.  The row sums are taken in the PV phase.
 __device__ __forceinline__ void fwd_tile_p(const FwdCtx &x, const f32x16 &st, int s0, float mn) {
   const int half = x.w.l32 >> 4;
@@ -116,51 +121,64 @@ __device__ __forceinline__ void fwd_tile_p(const FwdCtx &x, const f32x16 &st, in
   for (int j = 0; j < 8; ++j)
     pk[j] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * j], x.c, -mn)),
                         __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * j + 1], x.c, -mn)));
-  char *prow = x.sP + (s0 + half) * kSlotStride + slot_store_offset(x.w);
+  char *prow = x.sP + ((x.sbase + s0 + half) & (kFwdSlots - 1)) * kSlotStride + slot_store_offset(x.w);
 #pragma unroll
   for (int j = 0; j < 4; ++j) *(u32x2 *)(prow + 16 * j) = u32x2{pk[2 * j], pk[2 * j + 1]};
 }
 
-// LDS operands of one pair of the S phase, read ahead of its MFMAs.
-struct FwdPair {
-  bf16x8 q[8];
-  float mn;
-  int u0, u1;
-  bool two;
-};
-
-// Pops the next pair of units from ms and issues its LDS reads (Q rows, references).
-__device__ __forceinline__ void fwd_pair_load(const FwdCtx &x, FwdPair &pr, uint32_t &ms) {
-  pr.u0 = pop_unit(ms);
-  pr.two = ms != 0;
-  pr.u1 = pr.two ? pop_unit(ms) : pr.u0;
-  load_pair_rows_padded(pr.q, x.sQ, pr.u0, pr.u1, x.w);
-  pr.mn = x.sM[((x.w.l32 < 16) ? pr.u0 : pr.u1) * 16 + x.w.l16];
+// B operand of a pair's tile (load_pair_rows_padded), addressed from the lane's base
+// and uniform unit offsets.
+__device__ __forceinline__ void fwd_pair_rows(const FwdCtx &x, bf16x8 (&q)[8], int u0, int u1) {
+  const int o0 = u0 * (16 * kUnitRow), o1 = u1 * (16 * kUnitRow);
+  const char *row = x.qrow + (x.lo ? o0 : o1);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) q[ks] = *(const bf16x8 *)(row + 32 * ks);
 }
 
-// S phase of one step (units mr): pairs in unit order at slots 0, 2, 4, ...  Once a
-// pair's MFMAs are issued (they have read their operands), the same registers are
-// refilled with the next pair's Q rows, which then arrive behind the MFMAs and the
-// current pair's softmax.  MASKED: the step's block is the diagonal block of some unit;
-// otherwise no key needs the causal mask and the pair loop carries no mask code (whose
-// divergent select would move every score tile out of the accumulation registers and
-// back).
+// This lane's column reference for the pair (u0, u1).
+__device__ __forceinline__ float fwd_pair_ref(const FwdCtx &x, int u0, int u1) {
+  return x.mrow[x.lo ? 16 * u0 : 16 * u1];
+}
+
+// The first pair of unit mask m (u1 = u0 for a lone unit).
+__device__ __forceinline__ void fwd_first_pair(uint32_t m, int &u0, int &u1) {
+  u0 = __builtin_ctz(m);
+  const uint32_t r = m & (m - 1);
+  u1 = r ? __builtin_ctz(r) : u0;
+}
+
+// S phase of one step (units mr): pairs in unit order at slots 0, 2, 4, ...  q holds the
+// first pair's Q rows (read at the end of the previous step).  Once a pair's MFMAs are
+// issued (they have read their operands), the same registers are refilled with the
+// next pair's Q rows, which then arrive behind the MFMAs and the current pair's
+// softmax.  MASKED: the step's block is the diagonal block of some unit; otherwise no
+// key needs the causal mask and the pair loop carries no mask code (whose divergent
+// select would move every score tile out of the accumulation registers and back).
 template <bool MASKED>
-__device__ __forceinline__ void fwd_scores(const FwdCtx &x, const bf16x8 (&k)[8], uint32_t mr, int b,
-                                           uint32_t dmask) {
-  FwdPair pr;
+__device__ __forceinline__ void fwd_scores(const FwdCtx &x, const bf16x8 (&k)[8], bf16x8 (&q)[8], uint32_t mr,
+                                           int b, uint32_t dmask) {
   uint32_t ms = mr;
-  fwd_pair_load(x, pr, ms);
+  int u0 = pop_unit(ms);
+  int u1 = ms ? pop_unit(ms) : u0;
+  float mn = fwd_pair_ref(x, u0, u1);
   for (int s0 = 0;; s0 += 2) {
-    const int u0 = pr.u0, u1 = pr.u1;
-    const float mn = pr.mn;
     const bool diag = fwd_tile_diag(dmask, u0, u1);
-    f32x16 st = tile32(k, pr.q);
-    const bool more = ms != 0;
-    if (more) fwd_pair_load(x, pr, ms);
+    f32x16 st = tile32(k, q);
+    // the next pair (pops kept in scalar registers)
+    const uint32_t m0 = (uint32_t)uniform((int)ms);
+    const bool more = m0 != 0;
+    const int n0 = more ? uniform(__builtin_ctz(m0)) : u0;
+    const uint32_t m1 = (uint32_t)uniform((int)(m0 & (m0 - 1)));
+    const int n1 = m1 ? uniform(__builtin_ctz(m1)) : n0;
+    ms = (uint32_t)uniform((int)(m1 & (m1 - 1)));
+    if (more) fwd_pair_rows(x, q, n0, n1);
+    const float nmn = fwd_pair_ref(x, n0, n1);
     if (MASKED) fwd_tile_mask(x, st, u0, u1, b, diag);
     fwd_tile_p(x, st, s0, mn);
     if (!more) break;
+    u0 = n0;
+    u1 = n1;
+    mn = nmn;
   }
 }
 
@@ -185,14 +203,13 @@ __device__ __forceinline__ float fwd_frag_sum(const bf16x8 (&pf)[4]) {
 }
 
 // PV phase of one step: O^T[dims 32w.., heads] += V^T P^T for the nr units of mr,
-// whose P slots are their ranks in mr, and row sums of the same bf16 P values the
-// products use: the step's k-th unit is summed by wave k % 4, into ls[u] (this lane's
-// keys).  After a unit's MFMAs are issued,
-// the same registers are refilled with the next slot's fragments.
+// whose P slots are their ranks in mr on the ring, and row sums of the same bf16 P
+// values the products use: the step's k-th unit is summed by wave k % 4, into ls[u]
+// (this lane's keys).  pf holds the first unit's fragments (read by the caller ahead of
+// its wait for V); after a unit's MFMAs are issued, the same registers are refilled
+// with the next slot's fragments.
 __device__ __forceinline__ void fwd_pv(const FwdCtx &x, const bf16x8 (&v)[2][4], uint32_t mr, int nr,
-                                       f32x4 (&acc)[kFwdGroup][2], float (&ls)[kFwdGroup]) {
-  bf16x8 pf[4];
-  load_slot(pf, x.sP, 0, x.w);
+                                       bf16x8 (&pf)[4], f32x4 (&acc)[kFwdGroup][2], float (&ls)[kFwdGroup]) {
   int k = 0;
 #pragma unroll
   for (int u = 0; u < kFwdGroup; ++u) {
@@ -200,7 +217,7 @@ __device__ __forceinline__ void fwd_pv(const FwdCtx &x, const bf16x8 (&v)[2][4],
       fwd_pv_mfma(v, pf, acc[u]);
       if ((k & 3) == x.w.wave) ls[u] += fwd_frag_sum(pf);  // the step's k-th unit: wave k % 4
       k = uniform(k + 1);
-      load_slot(pf, x.sP, min(k, nr - 1), x.w);
+      load_slot(pf, x.sP, (x.sbase + min(k, nr - 1)) & (kFwdSlots - 1), x.w);
     }
   }
 }
@@ -289,10 +306,16 @@ __device__ __forceinline__ void fwd_pos_advance(FwdPos &q) {
 // One step of the walk over list entry a (position q) with the K rows and V^T slices of
 // its block in kc / vc; the next entry's are loaded into kn / vn.  seen: units whose
 // reference is set.  MAXPASS only folds the block maxima into sM.
+//
+// The P slots form a ring: each step's slots follow the previous step's.  The next
+// step's S phase may then start while other waves still read this step's slots in
+// their PV phase, unless the two steps' slots (the next step's spare slot of a lone
+// unit included) exceed the ring; only then does the step end with a barrier.
 template <bool MAXPASS>
-__device__ __forceinline__ void fwd_step(const FwdCtx &x, int a, FwdPos &q, const bf16x8 (&kc)[8],
+__device__ __forceinline__ void fwd_step(FwdCtx &x, int a, FwdPos &q, const bf16x8 (&kc)[8],
                                          const bf16x8 (&vc)[2][4], bf16x8 (&kn)[8], bf16x8 (&vn)[2][4],
-                                         f32x4 (&acc)[kFwdGroup][2], float (&ls)[kFwdGroup], uint32_t &seen) {
+                                         bf16x8 (&qf)[8], f32x4 (&acc)[kFwdGroup][2], float (&ls)[kFwdGroup],
+                                         uint32_t &seen) {
   const int b = q.b;
   const uint32_t m = q.m;
   const int nu = __popc(m);
@@ -320,34 +343,49 @@ __device__ __forceinline__ void fwd_step(const FwdCtx &x, int a, FwdPos &q, cons
   // ---- S phase: the step's units in pairs, this wave's keys (one slot per unit)
   fwd_load_k_half<1>(x, kn, q.bn);
   if (dmask & m)
-    fwd_scores<true>(x, kc, m, b, dmask);
+    fwd_scores<true>(x, kc, qf, m, b, dmask);
   else
-    fwd_scores<false>(x, kc, m, b, dmask);
+    fwd_scores<false>(x, kc, qf, m, b, dmask);
   lds_barrier();
   fwd_load_v_half<0>(x, vn, q.bn);
+  bf16x8 pf[4];
+  load_slot(pf, x.sP, x.sbase, x.w);
   WAIT_VMCNT(12);  // this step's V^T slices
   // ---- PV phase
-  fwd_pv(x, vc, m, nu, acc, ls);
+  fwd_pv(x, vc, m, nu, pf, acc, ls);
   fwd_load_v_half<1>(x, vn, q.bn);
-  lds_barrier();  // P slots are rewritten by the next step
+  {  // the next step's first pair of Q rows
+    int n0, n1;
+    fwd_first_pair(q.mn, n0, n1);
+    fwd_pair_rows(x, qf, n0, n1);
+  }
+  const int nn = __popc(q.mn);
+  if (nu + nn + (nn & 1) > kFwdSlots) lds_barrier();  // the next step's P slots overlap this step's
+  x.sbase = (x.sbase + nu) & (kFwdSlots - 1);
   fwd_pos_advance(q);
 }
 
 // The whole walk over the item's list.  seen0 = ~0 keeps the references already in
 // sM (the exact maxima of the max pass).
 template <bool MAXPASS>
-__device__ __forceinline__ void fwd_walk(const FwdCtx &x, f32x4 (&acc)[kFwdGroup][2], float (&ls)[kFwdGroup],
+__device__ __forceinline__ void fwd_walk(FwdCtx &x, f32x4 (&acc)[kFwdGroup][2], float (&ls)[kFwdGroup],
                                          uint32_t seen0) {
   if (x.nact <= 0) return;
-  bf16x8 k0[8], k1[8], v0[2][4], v1[2][4];
+  x.sbase = 0;
+  bf16x8 k0[8], k1[8], v0[2][4], v1[2][4], qf[8];
   uint32_t seen = seen0;
   FwdPos q;
   fwd_pos_init(x, q);
   fwd_load_k(x, k0, q.b);
-  if (!MAXPASS) fwd_load_v(x, v0, q.b);
+  if (!MAXPASS) {
+    fwd_load_v(x, v0, q.b);
+    int u0, u1;
+    fwd_first_pair(q.m, u0, u1);
+    fwd_pair_rows(x, qf, u0, u1);
+  }
   for (int a = 0; a < x.nact; a += 2) {
-    fwd_step<MAXPASS>(x, a, q, k0, v0, k1, v1, acc, ls, seen);
-    if (a + 1 < x.nact) fwd_step<MAXPASS>(x, a + 1, q, k1, v1, k0, v0, acc, ls, seen);
+    fwd_step<MAXPASS>(x, a, q, k0, v0, k1, v1, qf, acc, ls, seen);
+    if (a + 1 < x.nact) fwd_step<MAXPASS>(x, a + 1, q, k1, v1, k0, v0, qf, acc, ls, seen);
   }
 }
 
@@ -379,6 +417,9 @@ fwd_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
   x.list = plan_lists + (size_t)2 * kPlanMaxList * p;
   x.c = scale_log2e;
   x.sQ = sQ; x.sP = sP; x.sM = sM; x.sX = sX;
+  x.qrow = sQ + x.w.l16 * kUnitRow + 16 * x.w.hi;
+  x.mrow = sM + x.w.l16;
+  x.lo = x.w.l32 < 16;
   const int tid = x.w.tid;
 
   // Q rows of the item (16 rows of 256 B per unit) into sQ
