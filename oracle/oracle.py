@@ -352,3 +352,45 @@ def effective_flops(q2k, cu_seqlens, num_heads: int = 64, head_dim: int = 128, b
     fwd = 4.0 * head_dim * blk * rows_per_slot * slots
     bwd = 10.0 * head_dim * blk * rows_per_slot * slots
     return fwd, bwd, slots
+
+
+def index_select(IQ, IK, cu_seqlens, topk: int = 16, blk: int = 128, queries=None):
+    """Document-local top-k block selection of the indexer: the q2k the operator consumes.
+
+    [PR] Design: the indexer selects a document-local q2k for every (index head, query)
+    and may align index-K like the attention K; [PR] Supported scope: 4 index heads,
+    head dim 128, block 128, top-k 16; [PR] Testing: truncated top-16 support.  The pages
+    do not give the scoring rule.  The reading taken here: the score of document-local
+    block b for index head i and the query at document position p is the largest
+    <IQ[t, i], IK[j, i]> over the keys j of block b the query can see (j <= p); the
+    selection is the min(16, p // 128 + 1) causal blocks of highest score, ties going to
+    the smaller block id, listed in ascending id order with -1 in the unused slots.
+
+    IQ, IK: [T, 4, 128] (any float dtype; computed in fp64).  queries: optional compact
+    token ids to evaluate (default all).  Returns (q2k int32 [4, T, topk] with -1 rows
+    for tokens not evaluated, scores dict (i, t) -> fp64 block scores of t's causal
+    blocks) -- the scores let a caller judge near-ties at the selection boundary.
+    """
+    IQ = np.asarray(IQ, dtype=np.float64)
+    IK = np.asarray(IK, dtype=np.float64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T, HI, _ = IQ.shape
+    q2k = np.full((HI, T, topk), -1, dtype=np.int32)
+    scores = {}
+    want = np.arange(T) if queries is None else np.asarray(queries, dtype=np.int64)
+    doc_of = np.searchsorted(cu, np.arange(T), side="right") - 1
+    for t in want:
+        d = doc_of[t]
+        c0 = cu[d]
+        p = t - c0
+        nb = p // blk + 1
+        for i in range(HI):
+            s = np.empty(nb, dtype=np.float64)
+            for b in range(nb):
+                keys = IK[c0 + b * blk:c0 + min(b * blk + blk, p + 1), i, :]
+                s[b] = np.max(keys @ IQ[t, i, :])
+            order = sorted(range(nb), key=lambda b: (-s[b], b))[:topk]
+            sel = sorted(order)
+            q2k[i, t, :len(sel)] = sel
+            scores[(i, int(t))] = s
+    return q2k, scores
