@@ -176,6 +176,28 @@ def recorded_traffic(cfg, dq_mode):
     return r["bytes"]
 
 
+def time_index_select(M, WL, torch, cu, m, dev, reps=10):
+    """The indexer's block selection on the same layout (synthetic index-Q / index-K):
+    kept out of `value`, as the pages' timing excludes selection."""
+    T = int(cu[-1])
+    it = WL.make_index_tensors(T, 4242, device=dev)
+    q2k = torch.empty((4, T, 16), dtype=torch.int32, device=dev)
+    for _ in range(3):
+        m.select(it["IQ"], it["IK"], q2k)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        m.select(it["IQ"], it["IK"], q2k)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    # every causal (query, block) pair scored over all 128 keys: 2 * 128 * 128 flop
+    pairs = sum(int(p // 128) + 1 for d in range(len(cu) - 1) for p in range(int(cu[d + 1] - cu[d])))
+    tflop = 4 * pairs * 2.0 * 128 * 128 / 1e12
+    return {"ms": round(ms, 4), "tflop": round(tflop, 4), "tflops": round(tflop / (ms * 1e-3), 2),
+            "note": "not part of value: the pages time the operator without selection"}
+
+
 def copy_probe(mib):
     """A plain device copy of mib MiB, five times: what the HBM byte counters read for
     it calibrates them (read mib MiB, write mib MiB per launch)."""
@@ -303,6 +325,7 @@ def main():
                         "executed_tflop": round((3 if recompute else 1) * unit / 1e12, 4),
                         "frac_mfma_peak": round(unit / (kern_ms["dq"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)})
     traffic = recorded_traffic(args.config, args.dq_mode)
+    index_select = time_index_select(M, WL, torch, cu, m, dev)
 
     out = {
         "metric": "MSA fwd+bwd effective TFLOP/s + ms/layer at 16k packed tokens, 1 MI355X",
@@ -338,6 +361,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "avg_launch_ms": round(main_ms, 4), "traffic": traffic},
         "kernels": kernels,
+        "index_select": index_select,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_tokens)

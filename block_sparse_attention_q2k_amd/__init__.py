@@ -41,7 +41,7 @@ EXPORTS = ["msa_layout_host", "msa_csr_scratch_bytes", "msa_csr_cols_capacity", 
            "msa_tasks_bytes", "msa_bwd_scratch_bytes", "msa_default_grid", "msa_align_kv",
            "msa_build_k2q_csr", "msa_plan", "msa_forward", "msa_backward_preprocess",
            "msa_tasks_meta_offset", "msa_build_tasks", "msa_backward", "msa_status_string",
-           "msa_set_timing_events", "msa_build_k2q_csr_noalloc"]
+           "msa_set_timing_events", "msa_build_k2q_csr_noalloc", "msa_index_select"]
 
 
 def lib():
@@ -69,6 +69,7 @@ def lib():
             "msa_align_kv": (I, [P, P, LP, P, P, P, P, P]),
             "msa_build_k2q_csr": (I, [P, LP, P, P, P, P, Z, P]),
             "msa_build_k2q_csr_noalloc": (I, [P, LP, P, P, P, P]),
+            "msa_index_select": (I, [P, P, LP, P, P]),
             "msa_plan": (I, [LP, P, P, Z, P]),
             "msa_forward": (I, [P, P, P, LP, P, F, P, P, P]),
             "msa_backward_preprocess": (I, [P, P, I, P, P]),
@@ -230,6 +231,18 @@ def msa_build_k2q_csr_noalloc(q2k, layout, row_ptr, cols, status, stream=None):
                                                _ptr(status), _stream(stream)))
 
 
+def msa_index_select(IQ, IK, layout, q2k, stream=None):
+    """The indexer's block selection: q2k int32 [4, T, 16] from index-Q / index-K bf16
+    [T, 4, 128] (top-16 document-local causal blocks by their best visible key)."""
+    bf, _, i32, _ = _dt()
+    fn = "msa_index_select"
+    for n, t in (("IQ", IQ), ("IK", IK)):
+        _need(fn, n, t, bf, (layout.T, NUM_INDEX_HEADS, HEAD_DIM))
+    _need(fn, "q2k", q2k, i32, (NUM_INDEX_HEADS, layout.T, TOPK))
+    _gpu(fn, IQ=IQ, IK=IK, q2k=q2k)
+    _check(fn, lib().msa_index_select(_ptr(IQ), _ptr(IK), layout.ref(), _ptr(q2k), _stream(stream)))
+
+
 def msa_plan(layout, q2k, plan, stream=None):
     _need_q2k("msa_plan", q2k, layout)
     _need("msa_plan", "plan", plan, None)
@@ -342,6 +355,14 @@ class MSA:
         self.Kt = torch.empty_like(self.Kw)  # [4][W/128][128][128] transposed blocks
         self.Vt = torch.empty_like(self.Kw)
         self.delta = torch.empty((L.T, NUM_Q_HEADS), dtype=torch.float32, device=device)
+
+    def select(self, IQ, IK, q2k=None, stream=None):
+        """The indexer's block selection for this layout.  Returns q2k int32 [4, T, 16]."""
+        import torch
+        if q2k is None:
+            q2k = torch.empty((NUM_INDEX_HEADS, self.layout.T, TOPK), dtype=torch.int32, device=self.device)
+        msa_index_select(IQ, IK, self.layout, q2k, stream)
+        return q2k
 
     def forward(self, Q, K, V, q2k, scale, O=None, LSE=None, stream=None):
         """CSR + plan + K/V alignment + forward.  Returns (O, LSE)."""

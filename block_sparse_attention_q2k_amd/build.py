@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(BUILD, "libmsa.so")
-SOURCES = ["msa_abi.hip", "msa_index.hip", "msa_forward.hip", "msa_backward.hip",
+SOURCES = ["msa_abi.hip", "msa_index.hip", "msa_indexer.hip", "msa_forward.hip", "msa_backward.hip",
            "msa_backward_kv.hip", "msa_backward_dq.hip", "msa_backward_dqs.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-munsafe-fp-atomics",

@@ -187,6 +187,16 @@ int msa_align_kv(const msa_bf16 *K, const msa_bf16 *V, const msa_layout *layout,
   return launch_rc(host::align_kv(K, V, L, Kw, Vw, Kt, Vt, (hipStream_t)stream));
 }
 
+int msa_index_select(const msa_bf16 *IQ, const msa_bf16 *IK, const msa_layout *layout, int32_t *q2k,
+                     void *stream) {
+  LayoutArgs L;
+  int rc = check_layout(layout, &L);
+  if (!rc) rc = check_ptrs({IQ, IK, q2k});
+  if (!rc) rc = check_device();
+  if (rc) return rc;
+  return launch_rc(host::index_select(IQ, IK, L, q2k, (hipStream_t)stream));
+}
+
 int msa_build_k2q_csr(const int32_t *q2k, const msa_layout *layout, int32_t *row_ptr,
                       int32_t *cols, int32_t *status, void *scratch, size_t scratch_bytes,
                       void *stream) {

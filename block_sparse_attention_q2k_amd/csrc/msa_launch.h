@@ -22,6 +22,7 @@ struct TaskView {
 
 namespace host {
 hipError_t fill_u32(void *p, size_t n, uint32_t v, hipStream_t s);
+hipError_t index_select(const void *IQ, const void *IK, const LayoutArgs &L, int32_t *q2k, hipStream_t s);
 hipError_t align_kv(const void *K, const void *V, const LayoutArgs &L, void *Kw, void *Vw,
                     void *Kt, void *Vt, hipStream_t s);
 hipError_t build_csr(const int32_t *q2k, const LayoutArgs &L, int32_t *row_ptr, int32_t *cols,

@@ -155,6 +155,23 @@ int msa_align_kv(const msa_bf16 *K, const msa_bf16 *V, const msa_layout *layout,
                  msa_bf16 *Kw, msa_bf16 *Vw, msa_bf16 *Kt, msa_bf16 *Vt, void *stream);
 
 /* ---------------------------------------------------------------------------------
+ * Indexer block selection: the q2k the operator consumes (pull-request page, Design:
+ * the indexer selects a document-local q2k and may align index-K; Supported scope: 4
+ * index heads, head dim 128, block 128, top-k 16; Testing: truncated top-16 support).
+ * The pages do not state the scoring rule; this library's reading: the score of
+ * document-local block b for index head i and the query t at document position p
+ * (b <= p / 128) is the largest <IQ[t, i], IK[j, i]> over the keys j of block b with
+ * j <= p, accumulated in fp32 from the bf16 inputs.
+ *   IQ, IK: bf16 [T, 4, 128] compact (index-Q and index-K projections).
+ *   q2k: int32 [4, T, 16] output.  Row (i, t) lists the min(16, p / 128 + 1) blocks of
+ *   highest score in ascending id order, ties going to the smaller id, and -1 in the
+ *   remaining slots.  Every row of every document is written.
+ * Reads IQ and IK only; no scratch.  Argument errors as for every call.
+ * --------------------------------------------------------------------------------- */
+int msa_index_select(const msa_bf16 *IQ, const msa_bf16 *IK, const msa_layout *layout, int32_t *q2k,
+                     void *stream);
+
+/* ---------------------------------------------------------------------------------
  * q2k -> k2q CSR inversion (pull-request page, Design: forward-derived CSR; bindings
  * page: build_k2q_csr).
  *   q2k: int32 [4, T, 16].  Row r = i * NB + gb (NB = W / 128) lists the queries t

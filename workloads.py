@@ -223,6 +223,18 @@ def make_tensors(T, seed, num_heads=NUM_Q_HEADS, num_kv=NUM_KV_HEADS, head_dim=H
     return out
 
 
+def make_index_tensors(T, seed, num_index_heads=NUM_INDEX_HEADS, head_dim=HEAD_DIM, device="cpu"):
+    """bf16 index-Q, index-K (in that draw order) from float32 N(0,1): the indexer's
+    projections, [T, 4, 128] each."""
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    out = {}
+    for name in ("IQ", "IK"):
+        x = torch.randn((T, num_index_heads, head_dim), generator=g, dtype=torch.float32)
+        out[name] = x.to(torch.bfloat16).to(device)
+    return out
+
+
 def make_config(cfg: int, device="cpu"):
     """Full workload: structure and tensors (tensor seed 1000 + cfg)."""
     cu, q2k = make_structure(cfg)
