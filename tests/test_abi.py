@@ -100,8 +100,12 @@ def test_argument_errors_return_before_device_use(M):
         assert lib.msa_forward(a, a, a, L.ref(), a, ctypes.c_float(sc), a, a, None) == E["SHAPE"], sc
         assert lib.msa_backward(a, a, a, a, a, a, a, a, a, a, 256, L.ref(), ctypes.c_float(sc), 2, a, a, a, a,
                                 1 << 40, None) == E["SHAPE"], sc
+    assert lib.msa_index_select(a, null, L.ref(), a, None) == E["NULL"]
+    assert lib.msa_index_select(a, a, L.ref(), mis, None) == E["ALIGN"]
+    assert lib.msa_index_select(a, a, None, a, None) == E["NULL"]
     bad = FakeLayout(M, T=1000, W=1000)
     assert lib.msa_align_kv(a, a, bad.ref(), a, a, a, a, None) == E["SHAPE"]
+    assert lib.msa_index_select(a, a, bad.ref(), a, None) == E["SHAPE"]
     assert lib.msa_status_string(4) == b"buffer smaller than its size query"
 
 
@@ -135,6 +139,13 @@ def test_binding_refuses_tensors_the_kernels_would_overrun(M):
         call(LSE=np.zeros((T, 64), dtype=np.float32))
     with pytest.raises(ValueError, match="shape"):
         M.msa_backward_preprocess(Q, Q, T, torch.zeros((T, 63), dtype=f32))
+    IQ = torch.zeros((T, 4, 128), dtype=bf)
+    with pytest.raises(ValueError, match="shape"):
+        M.msa_index_select(IQ, torch.zeros((T, 4, 64), dtype=bf), L, q2k)
+    with pytest.raises(ValueError, match="dtype"):
+        M.msa_index_select(IQ, IQ, L, q2k.to(torch.int64))
+    with pytest.raises(ValueError, match="not on a GPU"):
+        M.msa_index_select(IQ, IQ, L, q2k)
     m = M.MSA([0, 300, 700], grid=8, device="cpu")
     with pytest.raises(RuntimeError, match="forward"):
         m.backward(Q, Q, Q, LSE, 0.1)

@@ -223,6 +223,20 @@ def make_tensors(T, seed, num_heads=NUM_Q_HEADS, num_kv=NUM_KV_HEADS, head_dim=H
     return out
 
 
+def make_long_q2k(cu, seed, topk=TOPK, blk=BLOCK, p_unused=0.1):
+    """Vectorized q2k for very long documents: per (index head, query) the diagonal block
+    and topk - 1 uniform draws from the causal blocks (with replacement, so ids may
+    repeat), each slot then set to -1 with probability p_unused."""
+    rng = np.random.default_rng(seed)
+    blk_t = _token_blocks(np.asarray(cu), blk).astype(np.int64)
+    T = len(blk_t)
+    q = np.empty((NUM_INDEX_HEADS, T, topk), dtype=np.int32)
+    q[:, :, 0] = blk_t
+    q[:, :, 1:] = (rng.random((NUM_INDEX_HEADS, T, topk - 1)) * (blk_t[None, :, None] + 1)).astype(np.int32)
+    q[rng.random((NUM_INDEX_HEADS, T, topk)) < p_unused] = -1
+    return q
+
+
 def make_index_tensors(T, seed, num_index_heads=NUM_INDEX_HEADS, head_dim=HEAD_DIM, device="cpu"):
     """bf16 index-Q, index-K (in that draw order) from float32 N(0,1): the indexer's
     projections, [T, 4, 128] each."""
