@@ -156,8 +156,8 @@ TRAFFIC_SOURCES = ["msa_abi.hip", "msa_backward.hip", "msa_backward_kv.hip", "ms
                    "msa_backward_dqs.hip", "msa_index.hip", "msa_walk.h", "msa_device.h", "msa_launch.h",
                    "../build.py"]
 TRAFFIC_RECORD = {"config": 2, "dq_mode": "stored",
-                  "sha256": "38e6e1dfbcc960038742884ef02822599d79556a0fca34ce676d55a428b6d81e",
-                  "bytes": 17028731056}  # read 12.510 GB + written 4.518 GB
+                  "sha256": "06cb6539084ac8465e2154837bca4e01d085f371584a36be522db7178c774785",
+                  "bytes": 17030676820}  # read 12.512 GB + written 4.519 GB
 
 
 def sources_digest():
