@@ -122,3 +122,23 @@ def test_index_select_full_size_sampled():
     qs = sorted(set(rng.integers(0, T, 240).tolist()) | set(range(T - 16, T)))
     ties = _check_rows(cu, tens["IQ"], tens["IK"], got, qs)
     say("  16k sampled rows at a score tie: %d of %d" % (ties, 4 * len(qs)))
+
+
+def test_selection_feeds_the_operator():
+    """The path from the indexer on: the GPU selection (checked against the oracle) drives
+    the forward and backward, whose outputs match the oracle given the same q2k."""
+    from _gpu_util import SCALE, check_close, check_lse, inputs64, run_gpu, to_np
+    cu = WL.cu_from_lengths([2600, 300, 129])
+    T = int(cu[-1])
+    it = WL.make_index_tensors(T, 615)
+    q2k = _run(cu, it["IQ"], it["IK"], q2k_init=-3)
+    assert _check_rows(cu, it["IQ"], it["IK"], q2k, list(range(T))) >= 0
+    tens = WL.make_tensors(T, 616)
+    _, out = run_gpu(cu, q2k, tens)
+    Qn, Kn, Vn, dOn = inputs64(tens)
+    rO, rL = OR.forward(Qn, Kn, Vn, q2k, cu, SCALE)
+    rdQ, rdK, rdV, _, _ = OR.backward(Qn, Kn, Vn, dOn, q2k, cu, SCALE)
+    check_close("O", to_np(out["O"]), rO)
+    check_lse(to_np(out["LSE"]), rL)
+    for name, r in (("dQ", rdQ), ("dK", rdK), ("dV", rdV)):
+        check_close(name, to_np(out[name]), r)
