@@ -103,14 +103,24 @@ def test_index_select_ties_and_repeat_calls():
     assert _check_rows(cu, tens["IQ"], tens["IK"], got2, list(range(0, T, 7)) + [T - 1]) >= 0
 
 
-def test_index_select_full_size_sampled():
-    """A 16,384-token document (128 blocks): every row is checked for form, and 256
-    sampled rows (the last block's included) against the oracle."""
-    cu = WL.cu_from_lengths([16384])
-    T = 16384
+@pytest.mark.parametrize("layout", ["single_16k", "packed_16k_row", "single_64k"])
+def test_index_select_full_size_sampled(layout):
+    """Full-size layouts: a 16,384-token document (128 blocks), the packed 16,384-token
+    row of several documents, and a 65,536-token document (512 blocks, the longest
+    walks).  Every row is checked for form, and about 256 sampled rows (the last
+    tokens and document starts included) against the oracle."""
+    if layout == "single_16k":
+        cu = WL.cu_from_lengths([16384])
+    elif layout == "packed_16k_row":
+        cu, _ = WL.make_structure(1)
+    else:
+        cu = WL.cu_from_lengths([65536])
+    cu = np.asarray(cu)
+    T = int(cu[-1])
     tens = WL.make_index_tensors(T, 901)
     got = _run(cu, tens["IQ"], tens["IK"], q2k_init=-9)
-    p = np.arange(T)
+    doc = np.searchsorted(cu, np.arange(T), side="right") - 1
+    p = np.arange(T) - cu[doc]
     n = np.minimum(TOPK, p // BLK + 1)
     for i in range(4):
         sel_ok = np.ones(T, bool)
@@ -119,9 +129,10 @@ def test_index_select_full_size_sampled():
             sel_ok &= np.where(k < n, (col >= 0) & (col <= p // BLK), col == -1)
         assert sel_ok.all()
     rng = np.random.default_rng(5)
-    qs = sorted(set(rng.integers(0, T, 240).tolist()) | set(range(T - 16, T)))
+    qs = set(rng.integers(0, T, 240).tolist()) | set(range(T - 8, T)) | set(cu[:-1].tolist())
+    qs = sorted(qs)[:300]
     ties = _check_rows(cu, tens["IQ"], tens["IK"], got, qs)
-    say("  16k sampled rows at a score tie: %d of %d" % (ties, 4 * len(qs)))
+    say("  %s: sampled rows at a score tie: %d of %d" % (layout, ties, 4 * len(qs)))
 
 
 def test_selection_feeds_the_operator():
