@@ -6,18 +6,20 @@
 // blocks in ascending order with the bit mask of the units that selected each block;
 // the kernels walk that list, loading every block once per item.
 //
-// Both kernels split a block's work over their 4 waves (one per SIMD) the same way:
-// wave w owns keys [32w, 32w + 32) of the score-like tiles (32 x 32 tiles of keys x
-// (2 units x 16 heads), 32x32x16 MFMAs with the key rows in registers and the units'
-// rows from LDS) and head dims [32w, 32w + 32) of the accumulating products (16x16x32
-// MFMAs, the transposed block rows in registers, the per-unit tiles from LDS slots).
+// Both kernels split a block's work over 4 waves the same way: wave w owns keys
+// [32w, 32w + 32) of the score-like tiles (32 x 32 tiles of keys x (2 units x 16
+// heads), 32x32x16 MFMAs with the key rows in registers and the units' rows from LDS)
+// and head dims [32w, 32w + 32) of the accumulating products (16x16x32 MFMAs, the
+// transposed block rows in registers, the per-unit tiles from LDS slots).  The dQ
+// kernel's 4 waves (one per SIMD) do both; the forward gives each to a role of its own
+// (4 score waves and 4 product waves, two waves per SIMD).
 #pragma once
 #include "msa_device.h"
 #include "msa_launch.h"
 
 namespace msa {
 
-constexpr int kWalkThreads = 256;  // 4 waves, one per SIMD
+constexpr int kWalkThreads = 256;  // 4 waves
 constexpr int kWalkWaves = kWalkThreads / 64;
 
 // Per-unit LDS slots ([16 heads][128 keys] bf16, P or dS) with rows padded to 272 B, so
