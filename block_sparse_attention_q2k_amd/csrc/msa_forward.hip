@@ -98,13 +98,14 @@ __device__ __forceinline__ bool fwd_tile_diag(uint32_t dmask, int u0, int u1) {
   return (((dmask >> u0) | (dmask >> u1)) & 1u) != 0;
 }
 
-// Causal mask of the tile on a diagonal block.
-__device__ __forceinline__ void fwd_tile_mask(const FwdCtx &x, f32x16 &st, int u0, int u1, int b, bool diag) {
+// Causal mask of a tile of key slice kw (keys 32 kw .. of the block) on a diagonal block.
+__device__ __forceinline__ void fwd_tile_mask(const FwdCtx &x, f32x16 &st, int u0, int u1, int b, bool diag,
+                                              int kw) {
   const int qpos = x.p0 + ((x.w.l32 < 16) ? u0 : u1);
   if (diag) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = b * kBlk + 32 * x.w.wave + 8 * (r >> 2) + 4 * x.w.hi + (r & 3);
+      const int key = b * kBlk + 32 * kw + 8 * (r >> 2) + 4 * x.w.hi + (r & 3);
       if (key > qpos) st[r] = -INFINITY;
     }
   }
@@ -182,7 +183,7 @@ __device__ __forceinline__ void fwd_scores(const FwdCtx &x, const bf16x8 (&k)[8]
     ms = (uint32_t)uniform((int)(m1 & (m1 - 1)));
     if (more) fwd_pair_rows(x, q, n0, n1);
     const float nmn = fwd_pair_ref(x, n0, n1);
-    if (MASKED) fwd_tile_mask(x, st, u0, u1, b, diag);
+    if (MASKED) fwd_tile_mask(x, st, u0, u1, b, diag, x.w.wave);
     fwd_tile_p(x, st, s0, mn, u1 != u0);
     if (!more) break;
     u0 = n0;
@@ -231,25 +232,32 @@ __device__ __forceinline__ void fwd_pv(const FwdCtx &x, const bf16x8 (&v)[2][4],
   }
 }
 
-// References of the units in `units` (a unit's first block): the maximum over score
-// wave 0's 32 keys (keys 0..31) of block b, published to the score waves through sM
+// Key slice 0 (keys 0..31) of block b as tile operands, in every score wave.
+__device__ __forceinline__ void fwd_load_slice0(const FwdCtx &x, bf16x8 (&k)[8], int b) {
+  WalkLane w0 = x.w;
+  w0.wave = 0;
+  load_key_rows(k, x.Kw, fwd_gblk(x, b), w0);
+}
+
+// References of the units in `units` (a unit's first block): the maximum over key
+// slice 0 (keys 0..31) of block b, whose rows k0 every score wave holds; the unit pairs
+// are shared out over the score waves, and the maxima reach all of them through sM
 // (the barrier is taken by every wave of the workgroup).
-__device__ __forceinline__ void fwd_references(const FwdCtx &x, const bf16x8 (&k)[8], uint32_t units,
-                                               int b) {
-  if (x.w.wave == 0) {
-    while (units) {
-      const int u0 = pop_unit(units);
-      const bool two = units != 0;
-      const int u1 = two ? pop_unit(units) : u0;
-      bf16x8 q[8];
-      load_pair_rows_padded(q, x.sQ, u0, u1, x.w);
-      const bool diag = fwd_tile_diag(diag_units(x.p0, b), u0, u1);
-      f32x16 st = tile32(k, q);
-      fwd_tile_mask(x, st, u0, u1, b, diag);
-      const float mx = fwd_tile_max(st) * x.c;
-      const int u = (x.w.l32 < 16) ? u0 : u1;
-      if (x.w.hi == 0 && (x.w.l32 < 16 || two)) x.sM[u * 16 + x.w.l16] = mx;
-    }
+__device__ __forceinline__ void fwd_references(const FwdCtx &x, const bf16x8 (&k0)[8], uint32_t units, int b) {
+  int p = 0;
+  for (uint32_t us = units; us; ++p) {
+    const int u0 = pop_unit(us);
+    const bool two = us != 0;
+    const int u1 = two ? pop_unit(us) : u0;
+    if ((p & (kWalkWaves - 1)) != x.w.wave) continue;
+    bf16x8 q[8];
+    load_pair_rows_padded(q, x.sQ, u0, u1, x.w);
+    const bool diag = fwd_tile_diag(diag_units(x.p0, b), u0, u1);
+    f32x16 st = tile32(k0, q);
+    fwd_tile_mask(x, st, u0, u1, b, diag, 0);
+    const float mx = fwd_tile_max(st) * x.c;
+    const int u = (x.w.l32 < 16) ? u0 : u1;
+    if (x.w.hi == 0 && (x.w.l32 < 16 || two)) x.sM[u * 16 + x.w.l16] = mx;
   }
   lds_barrier();
 }
@@ -267,7 +275,7 @@ __device__ __forceinline__ void fwd_fold_max(const FwdCtx &x, const bf16x8 (&k)[
     load_pair_rows_padded(q, x.sQ, u0, u1, x.w);
     const bool diag = fwd_tile_diag(diag_units(x.p0, b), u0, u1);
     f32x16 st = tile32(k, q);
-    fwd_tile_mask(x, st, u0, u1, b, diag);
+    fwd_tile_mask(x, st, u0, u1, b, diag, x.w.wave);
     const float mx = fwd_tile_max(st) * x.c;
     const int u = (x.w.l32 < 16) ? u0 : u1;
     if (x.w.hi == 0 && (x.w.l32 < 16 || two)) sX[(x.w.wave * kFwdGroup + u) * 16 + x.w.l16] = mx;
@@ -351,7 +359,8 @@ __device__ __forceinline__ void fwd_pos_advance(const FwdCtx &x, FwdPos &q) {
 // in order: the references (if the step holds a unit's first block), the step's
 // hand-over.
 __device__ __forceinline__ void fwd_score_step(FwdCtx &x, FwdPos &q, const bf16x8 (&kc)[8], bf16x8 (&kn)[8],
-                                               bf16x8 (&qf)[8], uint32_t &seen) {
+                                               bf16x8 (&qf)[8], uint32_t &seen, bool first,
+                                               const bf16x8 (&ks0)[8]) {
   const int b = q.b;
   const uint32_t m = q.m;
   // The next block's K rows in two groups of four loads, the first at the start of
@@ -359,7 +368,16 @@ __device__ __forceinline__ void fwd_score_step(FwdCtx &x, FwdPos &q, const bf16x
   fwd_load_k_half<0>(x, kn, q.bn);
   WAIT_VMCNT(4);  // this step's K rows (issued in the previous step)
   const uint32_t fresh = m & ~seen;
-  if (fresh) fwd_references(x, kc, fresh, b);
+  if (fresh) {
+    if (first) {
+      fwd_references(x, ks0, fresh, b);  // key slice 0 of the first block, loaded with its K rows
+    } else {
+      bf16x8 k0[8];
+      fwd_load_slice0(x, k0, b);
+      WAIT_VMCNT(0);
+      fwd_references(x, k0, fresh, b);
+    }
+  }
   seen |= m;
   fwd_load_k_half<1>(x, kn, q.bn);
   const uint32_t dmask = diag_units(x.p0, b);
@@ -407,15 +425,19 @@ __device__ __forceinline__ void fwd_score_walk(FwdCtx &x, uint32_t seen0) {
   FwdPos q;
   fwd_pos_init(x, q);
   fwd_load_k(x, k0, q.b);
+  bf16x8 ks0[8];  // key slice 0 of the first block: its units' references
+  fwd_load_slice0(x, ks0, q.b);
   {
     int u0, u1;
     fwd_first_pair(q.m, u0, u1);
     fwd_pair_rows(x, qf, u0, u1);
   }
+  bool first = true;
   for (;;) {
-    fwd_score_step(x, q, k0, k1, qf, seen);
+    fwd_score_step(x, q, k0, k1, qf, seen, first, ks0);
+    first = false;
     if (q.m == 0u) break;
-    fwd_score_step(x, q, k1, k0, qf, seen);
+    fwd_score_step(x, q, k1, k0, qf, seen, false, ks0);
     if (q.m == 0u) break;
   }
   lds_barrier();  // the PV waves' last step
