@@ -152,7 +152,7 @@ def cpu_baseline(cfg, budget_tokens):
 # reading for a plain copy of known size; valid only for the build they were taken on:
 # sha256 over every library source the backward launches depend on (the forward's own
 # file excepted) and the build script with its compiler flags.
-TRAFFIC_SOURCES = ["msa_abi.hip", "msa_backward.hip", "msa_backward_kv.hip", "msa_backward_dq.hip",
+TRAFFIC_SOURCES = ["msa_abi.hip", "msa_backward.hip", "msa_backward_kv.hip", "msa_backward_kv2.hip", "msa_backward_dq.hip",
                    "msa_backward_dqs.hip", "msa_index.hip", "msa_walk.h", "msa_device.h", "msa_launch.h",
                    "../build.py"]
 TRAFFIC_RECORD = {"config": 2, "dq_mode": "stored",
@@ -313,7 +313,8 @@ def main():
         {"kernel": "fwd_kernel", "avg_ms": round(kern_ms["fwd"], 4), "algorithmic_tflop": round(2 * unit / 1e12, 4),
          "executed_tflop": round(2 * unit / 1e12, 4),
          "frac_mfma_peak": round(2 * unit / (kern_ms["fwd"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
-        {"kernel": "bwd_kv_kernel" if split else "bwd_kernel", "avg_ms": round(kern_ms["kv"], 4),
+        {"kernel": ("bwd_kv2_kernel" if mode == M.DQ_STORED else "bwd_kv_kernel") if split else "bwd_kernel",
+         "avg_ms": round(kern_ms["kv"], 4),
          "algorithmic_tflop": round((4 if split else 5) * unit / 1e12, 4),
          "executed_tflop": round((4 if split else 5) * unit / 1e12, 4),
          "frac_mfma_peak": round((4 if split else 5) * unit / (kern_ms["kv"] * 1e-3) / 1e12

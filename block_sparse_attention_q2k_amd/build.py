@@ -9,7 +9,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(BUILD, "libmsa.so")
 SOURCES = ["msa_abi.hip", "msa_index.hip", "msa_indexer.hip", "msa_forward.hip", "msa_backward.hip",
-           "msa_backward_kv.hip", "msa_backward_dq.hip", "msa_backward_dqs.hip"]
+           "msa_backward_kv.hip", "msa_backward_kv2.hip", "msa_backward_dq.hip",
+           "msa_backward_dqs.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-munsafe-fp-atomics",
          # no packed-fp32 VALU ops (v_pk_*_f32) in any generated code

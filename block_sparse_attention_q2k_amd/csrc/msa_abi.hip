@@ -305,8 +305,10 @@ int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, cons
     if (pool)
       e = host::backward_main(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dq_accum_mode, sc,
                               dk_pool, dv_pool, s);
+    else if (stored)
+      e = host::backward_kv2(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dk_pool, dv_pool, ds, s);
     else
-      e = host::backward_kv(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dk_pool, dv_pool, ds, s);
+      e = host::backward_kv(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dk_pool, dv_pool, nullptr, s);
   }
   if (e == hipSuccess) e = mark(3, s);
   if (!pool) {

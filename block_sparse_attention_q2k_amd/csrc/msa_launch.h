@@ -51,6 +51,10 @@ hipError_t backward_kv(const void *Q, const void *Kw, const void *Vw, const void
                        const float *LSE, const float *delta, const void *tasks,
                        const LayoutArgs &L, int grid, float scale, float *dk_pool, float *dv_pool,
                        void *dS, hipStream_t s);
+// The same products for MSA_DQ_STORED (dS stored) with score and accumulate waves.
+hipError_t backward_kv2(const void *Q, const void *Kw, const void *Vw, const void *dO, const float *LSE,
+                        const float *delta, const void *tasks, const LayoutArgs &L, int grid, float scale,
+                        float *dk_pool, float *dv_pool, void *dS, hipStream_t s);
 hipError_t backward_dqs(const void *dS, const void *Kt, const int32_t *q2k, const LayoutArgs &L,
                         const void *plan, float scale, void *dQ, hipStream_t s);
 hipError_t backward_dq(const void *Q, const void *dO, const void *Kw, const void *Vw, const void *Kt,
