@@ -129,21 +129,29 @@ struct Kv2Stage {
   u32x4 q[2], o[2];
   f32x4 s;
 };
+// LEAD: the first accumulate wave, which also moves LSE and delta (a template argument,
+// so that each wave's code has no conditional load and its memory waits stay exact).
+template <bool LEAD>
 __device__ __forceinline__ void kv2_gather_load(Kv2Stage &st, int i, int t0, int t1, const uint16_t *__restrict__ Q,
                                                 const uint16_t *__restrict__ dO, const float *__restrict__ LSE,
                                                 const float *__restrict__ Delta, int at) {
+  // chunks at and at + 256 share the head (rq % 16) and the chunk, so one lane offset
+  // serves both; the row base is wave-uniform
+  const int hh = (at >> 4) & 15;
+  const unsigned off = (unsigned)(hh * kD + (((at & 15) ^ kv2_f(hh)) << 3)) * 2u;  // bytes
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int ci = at + 256 * j, rq = ci >> 4, hh = rq & 15;
     const int t = j ? t1 : t0;  // rows 0..15: query 2 q, 16..31: query 2 q + 1
-    const size_t src = ((size_t)t * kH + kHPI * i + hh) * kD + (((ci & 15) ^ kv2_f(hh)) << 3);
-    st.q[j] = *(const u32x4 *)(Q + src);
-    st.o[j] = *(const u32x4 *)(dO + src);
+    const size_t base = ((size_t)t * kH + kHPI * i) * kD;
+    st.q[j] = *(const u32x4 *)((const char *)(Q + base) + off);
+    st.o[j] = *(const u32x4 *)((const char *)(dO + base) + off);
   }
-  const int m = at & 7;
-  const int ts = (m >> 2) ? t1 : t0;
-  const float *sb = (at & 8) ? Delta : LSE;
-  st.s = *(const f32x4 *)(sb + (size_t)ts * kH + kHPI * i + 4 * (m & 3));
+  if constexpr (LEAD) {  // lanes 0..15 are used
+    const int m = at & 7;
+    const int ts = (m >> 2) ? t1 : t0;
+    const float *sb = (at & 8) ? Delta : LSE;
+    st.s = *(const f32x4 *)(sb + (size_t)ts * kH + kHPI * i + 4 * (m & 3));
+  }
 }
 __device__ __forceinline__ void kv2_gather_store(char *slot, const Kv2Stage &st, int at) {
 #pragma unroll
@@ -227,6 +235,10 @@ __device__ __forceinline__ void kv2_score(Kv2Score &s, const Kv2Ids &D, int qtr,
       s.kf[ks] = *(const bf16x8 *)(Kw + kfr + ks * 512);
       s.vf[ks] = *(const bf16x8 *)(Vw + kfr + ks * 512);
     }
+    // wait here, on this rare path: the compiler then sees the K / V registers complete on
+    // both paths and puts no wait after the join, where it would also wait for the
+    // previous phase's dS stores
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   }
   const lds_char *lq = (const lds_char *)sl;
   f32x16 sacc, pacc;
@@ -360,7 +372,7 @@ struct Kv2Ctx {
 // ids: the score waves' row g; for the accumulate waves, the row whose quarters they
 // gather in this row's phases (g + 1, or the last row) and prev: row g - 1 (its last
 // quarter is accumulated in phase 4 g).
-template <int QTR, bool SCORE>
+template <int QTR, bool SCORE, bool LEAD>
 __device__ __forceinline__ void kv2_phase(Kv2Ctx &x, int g, const Kv2Ids &ids, const Kv2Ids &prev,
                                           const Kv2Ids &gat, Kv2Stage (&stg)[2], int &dstg, Kv2Score &s,
                                           Kv2Acc &a,
@@ -375,13 +387,13 @@ __device__ __forceinline__ void kv2_phase(Kv2Ctx &x, int g, const Kv2Ids &ids, c
   const int n = 4 * g + QTR;
   if constexpr (!SCORE) {
     if (n >= 2) kv2_gather_store(x.slots + ((n + 2) % kKv2Slots) * kKv2SlotBytes, stg[QTR & 1], x.tid - 256);
-    if (QTR == 2 && x.wave == 0 && x.lane < kKv2Desc)
+    if (LEAD && QTR == 2 && x.lane < kKv2Desc)
       x.desc[((g + 2) & 3) * kKv2Desc + x.lane] = kv2_desc_pad(dstg, x.lane, ds_spare);
     // quarter n + kKv2Ahead = quarter QTR of row g + 1 (gat); past the end, a valid
     // quarter (unused)
     const int qa = g + 1 < x.R.total ? QTR : 3;
-    kv2_gather_load(stg[QTR & 1], gat.i, gat.t[2 * qa], gat.t[2 * qa + 1], Q, dO, LSE, Delta, x.tid - 256);
-    if (QTR == 0) dstg = kv2_desc_load(x.R, g + 2, meta, qrows, qpos, qtile, x.lane);
+    kv2_gather_load<LEAD>(stg[QTR & 1], gat.i, gat.t[2 * qa], gat.t[2 * qa + 1], Q, dO, LSE, Delta, x.tid - 256);
+    if (LEAD && QTR == 0) dstg = kv2_desc_load(x.R, g + 2, meta, qrows, qpos, qtile, x.lane);
   }
   if constexpr (SCORE) {
     if (n < x.nq)
@@ -445,14 +457,14 @@ bwd_kv2_kernel(uint16_t *__restrict__ dS, const uint16_t *__restrict__ Q, const 
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         Kv2Stage t;
-        kv2_gather_load(t, d0.i, d0.t[2 * q], d0.t[2 * q + 1], Q, dO, LSE, Delta, tid - 256);
+        kv2_gather_load<true>(t, d0.i, d0.t[2 * q], d0.t[2 * q + 1], Q, dO, LSE, Delta, tid - 256);
         kv2_gather_store(slots + q * kKv2SlotBytes, t, tid - 256);
       }
     }
   }
   __syncthreads();
   int dstg = 0;
-#define KV2_PHASES(SC)                                                                                      \
+#define KV2_PHASES(SC, LD)                                                                                      \
   for (int g = 0; g < x.R.total; ++g) {                                                                     \
     Kv2Ids ids, prev, gat;                                                                                  \
     kv2_ids(gat, desc + (min(g + 1, x.R.total - 1) & 3) * kKv2Desc, x.lane);                               \
@@ -460,13 +472,13 @@ bwd_kv2_kernel(uint16_t *__restrict__ dS, const uint16_t *__restrict__ Q, const 
       kv2_ids(ids, desc + (g & 3) * kKv2Desc, x.lane);                                                      \
     else                                                                                                    \
       kv2_ids(prev, desc + ((g + 3) & 3) * kKv2Desc, x.lane);                                               \
-    kv2_phase<0, SC>(x, g, ids, prev, gat, stg, dstg, s, a, Q, dO, LSE, Delta, dS, Kw, Vw, meta, qrows, qpos, qtile, cu_ws, \
+    kv2_phase<0, SC, LD>(x, g, ids, prev, gat, stg, dstg, s, a, Q, dO, LSE, Delta, dS, Kw, Vw, meta, qrows, qpos, qtile, cu_ws, \
                      ndocs, NB, scale_log2e, scale, dk_pool, dv_pool, ds_spare);                           \
-    kv2_phase<1, SC>(x, g, ids, prev, gat, stg, dstg, s, a, Q, dO, LSE, Delta, dS, Kw, Vw, meta, qrows, qpos, qtile, cu_ws, \
+    kv2_phase<1, SC, LD>(x, g, ids, prev, gat, stg, dstg, s, a, Q, dO, LSE, Delta, dS, Kw, Vw, meta, qrows, qpos, qtile, cu_ws, \
                      ndocs, NB, scale_log2e, scale, dk_pool, dv_pool, ds_spare);                           \
-    kv2_phase<2, SC>(x, g, ids, prev, gat, stg, dstg, s, a, Q, dO, LSE, Delta, dS, Kw, Vw, meta, qrows, qpos, qtile, cu_ws, \
+    kv2_phase<2, SC, LD>(x, g, ids, prev, gat, stg, dstg, s, a, Q, dO, LSE, Delta, dS, Kw, Vw, meta, qrows, qpos, qtile, cu_ws, \
                      ndocs, NB, scale_log2e, scale, dk_pool, dv_pool, ds_spare);                           \
-    kv2_phase<3, SC>(x, g, ids, prev, gat, stg, dstg, s, a, Q, dO, LSE, Delta, dS, Kw, Vw, meta, qrows, qpos, qtile, cu_ws, \
+    kv2_phase<3, SC, LD>(x, g, ids, prev, gat, stg, dstg, s, a, Q, dO, LSE, Delta, dS, Kw, Vw, meta, qrows, qpos, qtile, cu_ws, \
                      ndocs, NB, scale_log2e, scale, dk_pool, dv_pool, ds_spare);                           \
   }
   // each role runs its own loop, so that only its own state is live in it
@@ -477,7 +489,7 @@ bwd_kv2_kernel(uint16_t *__restrict__ dS, const uint16_t *__restrict__ Q, const 
     s.bucket = -1;
     s.kbase = 0;
     kv2_score_ops(s, slots, x.lane);  // quarter 0
-    KV2_PHASES(true)
+    KV2_PHASES(true, false)
   } else {
     Kv2Stage stg[2];
     Kv2Score s;  // unused
@@ -486,7 +498,11 @@ bwd_kv2_kernel(uint16_t *__restrict__ dS, const uint16_t *__restrict__ Q, const 
     for (int nd = 0; nd < 4; ++nd)
 #pragma unroll
       for (int e = 0; e < 16; ++e) a.dk[nd][e] = a.dv[nd][e] = 0.f;
-    KV2_PHASES(false)
+    if (x.wave == 0) {
+      KV2_PHASES(false, true)
+    } else {
+      KV2_PHASES(false, false)
+    }
     // the last quarter (phase nq)
     const int m = x.nq - 1;
     Kv2Ids last;
