@@ -308,7 +308,7 @@ int msa_backward(const msa_bf16 *Q, const msa_bf16 *Kw, const msa_bf16 *Vw, cons
     else if (stored)
       e = host::backward_kv2(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dk_pool, dv_pool, ds, s);
     else
-      e = host::backward_kv(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dk_pool, dv_pool, nullptr, s);
+      e = host::backward_kv(Q, Kw, Vw, dO, LSE, delta, tasks, L, grid, scale, dk_pool, dv_pool, s);
   }
   if (e == hipSuccess) e = mark(3, s);
   if (!pool) {

@@ -5,9 +5,9 @@
 // the block's 128 keys: S = Q K^T, P = exp(scale S - LSE) under the causal mask,
 // dP = dO V^T, dS = P (dP - delta), dV += P^T dO, dK += scale dS^T Q.  dK/dV
 // accumulate in registers over the consecutive rows of one bucket and are flushed
-// with fp32 atomics at the end of the bucket segment.  dQ is produced by a
-// query-parallel kernel: from the bf16 dS tiles this kernel stores (STORE_DS,
-// msa_backward_dqs.hip) or by recomputation (msa_backward_dq.hip).
+// with fp32 atomics at the end of the bucket segment.  This kernel serves the recompute
+// mode (MSA_DQ_RECOMPUTE), whose dQ the query-parallel kernel recomputes
+// (msa_backward_dq.hip); the stored-dS mode uses msa_backward_kv2.hip.
 //
 // Design (gfx950): persistent grid; workgroup c walks, per index head, the task rows
 // [cta[i][c], cta[i][c+1]).  Four waves, wave w owns keys [32w, 32w+32): K and V
@@ -30,8 +30,8 @@ namespace msa {
 
 constexpr int kKvThreads = 256;
 constexpr int kKvTile = 65536;               // Q tile 32 KB + dO tile 32 KB
-constexpr int kKvScalBytes = (2 * 128 + 8 + 8) * 4;  // lse2[128], delta[128], qpos[8], dS tile[8]
-constexpr int kKvScPos = 256, kKvScTile = 264;      // word offsets of qpos / dS tile indices
+constexpr int kKvScalBytes = (2 * 128 + 8) * 4;  // lse2[128], delta[128], qpos[8]
+constexpr int kKvScPos = 256;                   // word offset of qpos
 
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
@@ -201,11 +201,8 @@ __device__ __forceinline__ const lds_char *kv_opaque_lds(const lds_char *p) {
 }
 
 struct KvRowCtx {
-  uint16_t *dS;
   uint32_t vis;  // bit q: query q of the row sees this lane's key
   float c;       // scale * log2(e)
-  int dsoff;
-  int tix[kTileQ];  // dS tile of each query of the row (uniform)
   // this lane's LDS addresses: S/dP operand of k-step ks in quarter 0 of the Q tile (+8192
   // per quarter, +32768 for dO); DK operand rows 4 h + j16 / 4 (+8 for hi) of dims
   // 32 nd .. of k-step 0 (+4096 per k-step, +32768 for dO); LSE of rows 4 h .. (+4 per row,
@@ -277,11 +274,8 @@ __device__ __forceinline__ void kv_step_reads(const KvRowCtx &x, KvRegs &g, int 
 
 // Softmax chunk j of quarter SQ (registers 4 j .. 4 j + 3 of its S / dP accumulators:
 // rows 32 SQ + 8 j + 4 h + 0..3 of query 2 SQ + j / 2).  After chunks 1 and 3 the bf16
-// operands of query 2 SQ + j / 2 are complete; with STORE_DS they are also written to
-// its dS tile (this lane's key, tile positions 8 h .. + 7 = heads 4 h .. + 3 and 8 + 4 h
-// .. + 3; non-temporal: each tile is read once, by the dQ kernel, and should not displace
-// the Q/dO rows the gathers re-read from the caches).
-template <int SQ, int J, bool STORE_DS>
+// operands of query 2 SQ + j / 2 are complete.
+template <int SQ, int J>
 __device__ __forceinline__ void kv_sm_chunk(const KvRowCtx &x, KvRegs &g, int b) {
   constexpr int set = SQ & 1, sg = J >> 1;
   const bool seen = (x.vis >> (2 * SQ + sg)) & 1u;
@@ -298,9 +292,6 @@ __device__ __forceinline__ void kv_sm_chunk(const KvRowCtx &x, KvRegs &g, int b)
       g.pa[set][sg][e] = (__bf16)g.s[set][8 * sg + e];
       g.sa[set][sg][e] = (__bf16)g.p[set][8 * sg + e];
     }
-    if constexpr (STORE_DS)
-      __builtin_nontemporal_store(g.sa[set][sg],
-                                  (bf16x8 *)(x.dS + (size_t)x.tix[2 * SQ + sg] * (kBlk * 16) + x.dsoff));
   }
 }
 
@@ -328,14 +319,14 @@ struct KvState {
   int cur_r, kbase, gb;
   int r_row, nv_row;  // bucket and valid-query count of the row about to be computed
   float lse2, del;
-  int pos, qt;  // qt: stored-dS tile index of the next row's query tid (tid < 8)
+  int pos;
   int idv;      // ids of the next row (kv_ids_load)
 };
 
 // Step S of the row: reads of step S + 2 (buffer (S + 2) % 3), the 4 MFMAs of step S
 // (operands in buffer S % 3), its softmax chunk, and a quarter of the next row's gather
 // in the first step of each DK phase.
-template <int S, bool STORE_DS>
+template <int S>
 __device__ __forceinline__ void kv_step(const KvRowCtx &x, KvRegs &g, KvState &st, const KvRowIds &ids,
                                         const uint16_t *__restrict__ Q, const uint16_t *__restrict__ dO, int i,
                                         char *nxt, int tid) {
@@ -363,7 +354,7 @@ __device__ __forceinline__ void kv_step(const KvRowCtx &x, KvRegs &g, KvState &s
     }
   }
   constexpr int sq = kv_sm_quarter(S);
-  if constexpr (sq >= 0) kv_sm_chunk<sq, j, STORE_DS>(x, g, b);
+  if constexpr (sq >= 0) kv_sm_chunk<sq, j>(x, g, b);
   // next row's gather: parts 0, 1 loaded in steps 0, 2 and written to LDS in steps 14, 16;
   // parts 2, 3 loaded in steps 14, 16 and written in steps 28, 30
   if constexpr (S == 14) kv_gather_store<0>(nxt, tid, g.gq[0]);
@@ -378,27 +369,24 @@ __device__ __forceinline__ void kv_step(const KvRowCtx &x, KvRegs &g, KvState &s
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int S, bool STORE_DS>
+template <int S>
 __device__ __forceinline__ void kv_steps(const KvRowCtx &x, KvRegs &g, KvState &st, const KvRowIds &ids,
                                          const uint16_t *__restrict__ Q, const uint16_t *__restrict__ dO, int i,
                                          char *nxt, int tid) {
   if constexpr (S < 32) {
-    kv_step<S, STORE_DS>(x, g, st, ids, Q, dO, i, nxt, tid);
-    kv_steps<S + 1, STORE_DS>(x, g, st, ids, Q, dO, i, nxt, tid);
+    kv_step<S>(x, g, st, ids, Q, dO, i, nxt, tid);
+    kv_steps<S + 1>(x, g, st, ids, Q, dO, i, nxt, tid);
   }
 }
 
 // One task row: compute from tile `cur` (+ its scalars), prefetch row + 1 into `nxt`.
-template <bool STORE_DS>
 __device__ __forceinline__ void kv_row(
     KvState &st, int row, int hi, int i, char *cur, float *cur_sc, char *nxt, float *nxt_sc,
-    uint16_t *__restrict__ dS, const int32_t *__restrict__ qtile,
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw, const uint16_t *__restrict__ Vw,
     const uint16_t *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
     const i32x4 *__restrict__ meta, const int32_t *__restrict__ qrows,
     const int32_t *__restrict__ qpos, const int32_t *__restrict__ cu_ws, int ndocs, int NB,
-    float scale, float scale_log2e, float *__restrict__ dk_pool, float *__restrict__ dv_pool,
-    int ds_spare, int tid_in) {
+    float scale, float scale_log2e, float *__restrict__ dk_pool, float *__restrict__ dv_pool, int tid_in) {
   const int tid = kv_opaque(tid_in);
   const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
   const int j16 = lane & 15, G = l32 >> 4;
@@ -436,10 +424,7 @@ __device__ __forceinline__ void kv_row(
   // unused buffer, which keeps the compute block free of branches)
   KvRowIds ids;
   kv_ids_unpack(ids, st.idv, __builtin_amdgcn_readlane(st.idv, 17), lane);
-  if (more) {
-    if (tid < 128) kv_scalars(LSE, Delta, ids, i, tid, st.lse2, st.del, st.pos);
-    if (STORE_DS && tid < kTileQ) st.qt = qtile[(size_t)(row + 1) * kTileQ + tid];
-  }
+  if (more && tid < 128) kv_scalars(LSE, Delta, ids, i, tid, st.lse2, st.del, st.pos);
   // 3. compute.  Causal mask of this lane's key against the row's 8 queries, bit q set
   //    when query q sees it (never for padding queries, whose position is -1).
   const int kp = st.kbase + 32 * wave + l32;  // document-local position of this lane's key
@@ -452,27 +437,13 @@ __device__ __forceinline__ void kv_row(
   }
   KvRowCtx x;
   kv_row_addresses(x, cur, cur_sc, l32, h, j16, G);
-  x.dS = dS;
   x.vis = vis;
   x.c = scale_log2e;
-  x.dsoff = ds_key_swz(32 * wave + l32) * 16 + 8 * h;  // this lane's 8 heads of a dS tile
-  if (STORE_DS) {  // padding queries write the spare tile
-    const i32x4 t0 = *(const i32x4 *)((const int32_t *)cur_sc + kKvScTile);
-    const i32x4 t1 = *(const i32x4 *)((const int32_t *)cur_sc + kKvScTile + 4);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      x.tix[q] = __builtin_amdgcn_readfirstlane(t0[q] >= 0 ? t0[q] : ds_spare);
-      x.tix[4 + q] = __builtin_amdgcn_readfirstlane(t1[q] >= 0 ? t1[q] : ds_spare);
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < kTileQ; ++q) x.tix[q] = 0;
-  }
   KvRegs g;
   kv_step_reads<0>(x, g, 0);
   kv_step_reads<1>(x, g, 1);
   __builtin_amdgcn_sched_barrier(0);
-  kv_steps<0, STORE_DS>(x, g, st, ids, Q, dO, i, nxt, tid);
+  kv_steps<0>(x, g, st, ids, Q, dO, i, nxt, tid);
   // 4. end of this bucket's segment in this workgroup: flush dK/dV
   if (!more || r_next != r) {
     // register e of dvacc[nd]: key 32w + 8(e/4) + 4h + e%4, dim 32nd + l32
@@ -490,23 +461,20 @@ __device__ __forceinline__ void kv_row(
   }
   // 5. scalars of row + 1 -> LDS; everyone done with `cur` and done writing `nxt`
   if (more && tid < 128) kv_store_scalars(nxt_sc, tid, st.lse2, st.del, st.pos);
-  if (STORE_DS && more && tid < kTileQ) ((int32_t *)nxt_sc)[kKvScTile + tid] = st.qt;
   st.r_row = r_next;
   st.nv_row = __builtin_amdgcn_readlane(st.idv, 17);
   st.idv = idv2;
   kv_lds_barrier();
 }
 
-template <bool STORE_DS>
 __global__ void __launch_bounds__(kKvThreads, 1)
-bwd_kv_kernel(uint16_t *__restrict__ dS, const int32_t *__restrict__ qtile,
-              const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
+bwd_kv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
               const uint16_t *__restrict__ Vw, const uint16_t *__restrict__ dO,
               const float *__restrict__ LSE, const float *__restrict__ Delta,
               const int32_t *__restrict__ cta, const i32x4 *__restrict__ meta,
               const int32_t *__restrict__ qrows, const int32_t *__restrict__ qpos,
               const int32_t *__restrict__ cu_ws, int ndocs, int NB, int grid, float scale,
-              float scale_log2e, float *__restrict__ dk_pool, float *__restrict__ dv_pool, int ds_spare) {
+              float scale_log2e, float *__restrict__ dk_pool, float *__restrict__ dv_pool) {
   // two separate arrays: the compiler can then tell the tile being read from the one
   // being filled by the asynchronous gather and does not wait for the latter
   __shared__ __attribute__((aligned(16))) char tile0[kKvTile];
@@ -528,7 +496,6 @@ bwd_kv_kernel(uint16_t *__restrict__ dS, const int32_t *__restrict__ qtile,
       if (tid < 128) {
         kv_scalars(LSE, Delta, ids, i, tid, st.lse2, st.del, st.pos);
         kv_store_scalars(sc0, tid, st.lse2, st.del, st.pos);
-        if (STORE_DS && tid < kTileQ) ((int32_t *)sc0)[kKvScTile + tid] = qtile[(size_t)lo * kTileQ + tid];
       }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -540,11 +507,11 @@ bwd_kv_kernel(uint16_t *__restrict__ dS, const int32_t *__restrict__ qtile,
     }
     st.cur_r = -1;
     for (int row = lo; row < hi; row += 2) {
-      kv_row<STORE_DS>(st, row, hi, i, tile0, sc0, tile1, sc1, dS, qtile, Q, Kw, Vw, dO, LSE, Delta, meta,
-                       qrows, qpos, cu_ws, ndocs, NB, scale, scale_log2e, dk_pool, dv_pool, ds_spare, tid);
+      kv_row(st, row, hi, i, tile0, sc0, tile1, sc1, Q, Kw, Vw, dO, LSE, Delta, meta, qrows, qpos, cu_ws, ndocs,
+             NB, scale, scale_log2e, dk_pool, dv_pool, tid);
       if (row + 1 < hi)
-        kv_row<STORE_DS>(st, row + 1, hi, i, tile1, sc1, tile0, sc0, dS, qtile, Q, Kw, Vw, dO, LSE, Delta,
-                         meta, qrows, qpos, cu_ws, ndocs, NB, scale, scale_log2e, dk_pool, dv_pool, ds_spare, tid);
+        kv_row(st, row + 1, hi, i, tile1, sc1, tile0, sc0, Q, Kw, Vw, dO, LSE, Delta, meta, qrows, qpos, cu_ws,
+               ndocs, NB, scale, scale_log2e, dk_pool, dv_pool, tid);
     }
   }
 }
@@ -553,13 +520,12 @@ namespace host {
 hipError_t backward_kv(const void *Q, const void *Kw, const void *Vw, const void *dO,
                        const float *LSE, const float *delta, const void *tasks,
                        const LayoutArgs &L, int grid, float scale, float *dk_pool, float *dv_pool,
-                       void *dS, hipStream_t s) {
+                       hipStream_t s) {
   TaskView v = task_view(L, grid, const_cast<void *>(tasks));
-  auto kern = dS ? bwd_kv_kernel<true> : bwd_kv_kernel<false>;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kKvThreads), 0, s, (uint16_t *)dS, v.qtile, (const uint16_t *)Q,
+  hipLaunchKernelGGL(bwd_kv_kernel, dim3(grid), dim3(kKvThreads), 0, s, (const uint16_t *)Q,
                      (const uint16_t *)Kw, (const uint16_t *)Vw, (const uint16_t *)dO, LSE, delta,
                      v.cta, (const i32x4 *)v.meta, v.qrows, v.qpos, L.cu_ws, L.ndocs, L.NB, grid,
-                     scale, scale * kLog2e, dk_pool, dv_pool, L.T * kHI * kTopk);
+                     scale, scale * kLog2e, dk_pool, dv_pool);
   return hipGetLastError();
 }
 }  // namespace host

@@ -46,11 +46,11 @@ hipError_t backward_main(const void *Q, const void *Kw, const void *Vw, const vo
                          const float *LSE, const float *delta, const void *tasks,
                          const LayoutArgs &L, int grid, float scale, int mode, void *dq_pool,
                          float *dk_pool, float *dv_pool, hipStream_t s);
-// dS non-null: also store the dS tiles (MSA_DQ_STORED) at the tasks' tile indices.
+// dK/dV for MSA_DQ_RECOMPUTE (the dQ kernel recomputes S and dP).
 hipError_t backward_kv(const void *Q, const void *Kw, const void *Vw, const void *dO,
                        const float *LSE, const float *delta, const void *tasks,
                        const LayoutArgs &L, int grid, float scale, float *dk_pool, float *dv_pool,
-                       void *dS, hipStream_t s);
+                       hipStream_t s);
 // The same products for MSA_DQ_STORED (dS stored) with score and accumulate waves.
 hipError_t backward_kv2(const void *Q, const void *Kw, const void *Vw, const void *dO, const float *LSE,
                         const float *delta, const void *tasks, const LayoutArgs &L, int grid, float scale,
