@@ -23,11 +23,12 @@
 //     registers.
 // Within one wave, matrix products and vector arithmetic add up in time; across the two
 // waves of a SIMD the score wave's softmax issues while the accumulate wave's products
-// occupy the matrix unit.  One barrier per phase.  The Q / dO rows, LSE and delta of
-// each quarter are gathered by the accumulate waves (the lighter role), kKv2Ahead
+// occupy the matrix unit.  One barrier per phase.  The Q / dO rows of each quarter are
+// gathered by the accumulate waves (its LSE and delta by the first of them), kKv2Ahead
 // quarters ahead, into a ring of kKv2Slots LDS slots, staged through registers for two
-// phases; each task row's ids are read two rows ahead into a ring of descriptors.  With
-// two waves per SIMD the compiler keeps every accumulator in ordinary VGPRs.
+// phases; each task row's ids are read two rows ahead, by the first accumulate wave, into
+// a ring of descriptors.  With two waves per SIMD the compiler keeps every accumulator in
+// ordinary VGPRs.
 #include "msa_walk.h"  // uniform()
 
 namespace msa {
