@@ -108,6 +108,32 @@ def test_backward_parity_grids(grid):
     check_close("dV", to_np(out["dV"]), dV)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_parity_random_layouts(seed):
+    """Seeded random layouts (1-4 documents of 1-1,000 tokens, a random selection rule,
+    slots scattered) at a random grid: the forward and the default backward against the
+    oracle.  The grid changes how many task rows each workgroup of the KV kernel walks,
+    and so which of its ring slots and descriptor rows wrap."""
+    rng = np.random.default_rng(7000 + seed)
+    lens = [int(v) for v in rng.integers(1, 1001, int(rng.integers(1, 5)))]
+    rule = str(rng.choice(["uniform", "sink", "local_decay", "zipf"]))
+    grid = int(rng.choice([1, 3, 13, 64, 256, 999]))
+    say("case random layout", seed, lens, rule, "grid", grid)
+    cu, q2k = WL.make_custom(lens, rule, 7100 + seed)
+    q2k = WL.scatter_unused(q2k, 7200 + seed)
+    tens = WL.make_tensors(int(cu[-1]), 7300 + seed)
+    m, out = run_gpu(cu, q2k, tens, mode=3, grid=grid)
+    assert check_structures(m, cu, q2k) == 0
+    Q, K, V, dO = inputs64(tens)
+    O, LSE = OR.forward(Q, K, V, q2k, cu, SCALE)
+    check_close("O", to_np(out["O"]), O)
+    check_lse(to_np(out["LSE"]), LSE)
+    dQ, dK, dV, _, _ = OR.backward(Q, K, V, dO, q2k, cu, SCALE)
+    check_close("dQ", to_np(out["dQ"]), dQ)
+    check_close("dK", to_np(out["dK"]), dK)
+    check_close("dV", to_np(out["dV"]), dV)
+
+
 @pytest.mark.parametrize("scale", [0.03, 0.3])
 def test_parity_other_scales(scale):
     """Softmax scales other than 1/sqrt(128): the scale enters the exponents, the dK
