@@ -12,15 +12,17 @@
 //
 // Design (gfx950): persistent grid of 8-wave workgroups, two waves per SIMD.  A
 // workgroup's task rows (over the four index heads) form a sequence of quarters
-// (2 queries x 16 heads = 32 rows), one per phase.  Waves w and 4 + w (the hardware
-// puts them on one SIMD) own keys [32w, 32w + 32) of the bucket's block:
+// (2 queries x 16 heads = 32 rows), one per phase.  Waves w and 4 + w share a SIMD (the
+// hardware puts them on one); score wave w owns keys [32w, 32w + 32) of the bucket's
+// block, accumulate wave 4 + w dims [32w, 32w + 32):
 //   score wave w: in phase n, S and dP of quarter n (32x32x16 MFMAs, M = the quarter's
 //     rows from LDS, N = the wave's keys, K / V rows in registers), the softmax (P and
 //     dS), the dS tile stores, and P / dS (bf16, as the accumulate wave's A operands)
 //     to an LDS exchange slot;
 //   accumulate wave 4 + w: in phase n, dV += P^T dO and dK += dS^T Q of quarter n - 1
-//     (P / dS from the exchange slot, dO / Q through transposing LDS reads), dK / dV in
-//     registers.
+//     for all 128 keys and dims [32w, 32w + 32) (P / dS of the four score waves from
+//     their exchange slots, dO / Q through transposing LDS reads, each read once per
+//     k-step for all four key tiles), dK / dV in registers.
 // Within one wave, matrix products and vector arithmetic add up in time; across the two
 // waves of a SIMD the score wave's softmax issues while the accumulate wave's products
 // occupy the matrix unit.  One barrier per phase.  The Q / dO rows of each quarter are
@@ -296,43 +298,50 @@ __device__ __forceinline__ void kv2_score(Kv2Score &s, const Kv2Ids &D, int qtr,
 
 // ---- accumulate waves
 struct Kv2Acc {
-  f32x16 dk[4], dv[4];  // this wave's 32 keys x dims 32 nd ..: register e = key 8 (e / 4) + 4 h + e % 4
+  // all 128 keys x this wave's 32 dims: dk[kt] / dv[kt] hold keys 32 kt .., register e =
+  // key 32 kt + 8 (e / 4) + 4 h + e % 4, lane l32 = dim 32 w + l32
+  f32x16 dk[4], dv[4];
 };
 
-// dV += P^T dO and dK += dS^T Q of the quarter in slot sl with P / dS from xs; then, if
-// the row described by D ends its bucket segment and this is its last quarter, the
-// flush of dK / dV.
+// dV += P^T dO and dK += dS^T Q of the quarter in slot sl, with P / dS of the four score
+// waves (key tiles kt) from the exchange slots xs0 + kt kKv2XBytes; then, if the row
+// described by D ends its bucket segment and this is its last quarter, the flush of dK /
+// dV.  Accumulate wave w owns dims [32 w, 32 w + 32): the B operands (Q / dO with rows as
+// the contraction index, through transposing LDS reads) are read once per k-step and
+// serve all four key tiles; the A operands are the score waves' bf16 P / dS registers,
+// 16-byte reads.
 __device__ __forceinline__ void kv2_accumulate(Kv2Acc &a, const Kv2Ids &D, bool last_qtr, const char *sl,
-                                               const char *xs, int NB, float scale, float *__restrict__ dk_pool,
+                                               const char *xs0, int NB, float scale, float *__restrict__ dk_pool,
                                                float *__restrict__ dv_pool, int wave, int lane) {
   const int l32 = lane & 31, h = lane >> 5, j16 = lane & 15, G = l32 >> 4;
-  const bf16x8 pa0 = *(const bf16x8 *)(xs + (0 * 64 + lane) * 16);
-  const bf16x8 pa1 = *(const bf16x8 *)(xs + (1 * 64 + lane) * 16);
-  const bf16x8 sa0 = *(const bf16x8 *)(xs + (2 * 64 + lane) * 16);
-  const bf16x8 sa1 = *(const bf16x8 *)(xs + (3 * 64 + lane) * 16);
   const lds_char *lq = (const lds_char *)sl;
-  // Iteration it = (ks, nd) = (it / 4, it % 4): rows 16 ks .. 16 ks + 15 of the quarter
-  // (query ks), dims 32 nd ..  B operands with rows as the contraction index: lane
-  // (l32, h) gets dims 32 nd + l32 of rows 16 ks + 8 hi + 4 h + 0..3 (hi = 0, 1),
-  // matching the row order of the P / dS registers.  The operands of iteration it + 1
-  // are read before the MFMAs of iteration it; fences keep the compiler from reading
-  // further ahead (which would need more registers than the wave has).
+  // B operands of k-step ks: lane (l32, h) gets dims 32 w + l32 of rows 16 ks + 8 hi +
+  // 4 h + 0..3 (hi = 0, 1), matching the row order of the P / dS registers
   bf16x8 ob[2], qb[2];
-  auto rd = [&](int it, int b) {
-    const int ks = it >> 2, nd = it & 3;
-    const int c0 = 32 * nd + 16 * G + 4 * (j16 & 3);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int c0 = 32 * wave + 16 * G + 4 * (j16 & 3);
     const uint32_t r0 = kv2_swz(16 * ks + 4 * h + (j16 >> 2), c0 * 2);
     const uint32_t r1 = kv2_swz(16 * ks + 4 * h + (j16 >> 2) + 8, c0 * 2);
-    ob[b] = cat8(lds_read_tr(lq, kKv2Half + r0), lds_read_tr(lq, kKv2Half + r1));
-    qb[b] = cat8(lds_read_tr(lq, r0), lds_read_tr(lq, r1));
+    ob[ks] = cat8(lds_read_tr(lq, kKv2Half + r0), lds_read_tr(lq, kKv2Half + r1));
+    qb[ks] = cat8(lds_read_tr(lq, r0), lds_read_tr(lq, r1));
+  }
+  // Iteration it = (ks, kt) = (it / 4, it % 4); the A operands of iteration it + 1 are
+  // read before the MFMAs of iteration it.
+  bf16x8 pa[2], sa[2];
+  auto rd = [&](int it, int b) {
+    const int ks = it >> 2, kt = it & 3;
+    const char *xs = xs0 + kt * kKv2XBytes;
+    pa[b] = *(const bf16x8 *)(xs + ((0 + ks) * 64 + lane) * 16);
+    sa[b] = *(const bf16x8 *)(xs + ((2 + ks) * 64 + lane) * 16);
   };
   rd(0, 0);
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     if (it + 1 < 8) rd(it + 1, (it + 1) & 1);
-    const int nd = it & 3;
-    a.dv[nd] = mfma32(it < 4 ? pa0 : pa1, ob[it & 1], a.dv[nd]);
-    a.dk[nd] = mfma32(it < 4 ? sa0 : sa1, qb[it & 1], a.dk[nd]);
+    const int ks = it >> 2, kt = it & 3;
+    a.dv[kt] = mfma32(pa[it & 1], ob[ks], a.dv[kt]);
+    a.dk[kt] = mfma32(sa[it & 1], qb[ks], a.dk[kt]);
     __builtin_amdgcn_sched_barrier(0);
   }
   if (last_qtr && D.next != D.bucket) {
@@ -342,18 +351,18 @@ __device__ __forceinline__ void kv2_accumulate(Kv2Acc &a, const Kv2Ids &D, bool 
     // addresses would take registers from the whole walk
 #pragma unroll 1
     for (int e = 0; e < 16; e = uniform(e + 1)) {
-      const int key = 32 * wave + 8 * (e >> 2) + 4 * h + (e & 3);
-      const size_t o = ((size_t)(gb * kBlk + key) * kHKV + i) * kD + l32;
+      const int key = 8 * (e >> 2) + 4 * h + (e & 3);
+      const size_t o = ((size_t)(gb * kBlk + key) * kHKV + i) * kD + 32 * wave + l32;
 #pragma unroll
-      for (int nd = 0; nd < 4; ++nd) {
-        kv2_atomic_add(dk_pool + o + 32 * nd, scale * a.dk[nd][e]);
-        kv2_atomic_add(dv_pool + o + 32 * nd, a.dv[nd][e]);
+      for (int kt = 0; kt < 4; ++kt) {
+        kv2_atomic_add(dk_pool + o + (size_t)32 * kt * kHKV * kD, scale * a.dk[kt][e]);
+        kv2_atomic_add(dv_pool + o + (size_t)32 * kt * kHKV * kD, a.dv[kt][e]);
       }
     }
 #pragma unroll
-    for (int nd = 0; nd < 4; ++nd)
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) a.dk[nd][e] = a.dv[nd][e] = 0.f;
+      for (int e = 0; e < 16; ++e) a.dk[kt][e] = a.dv[kt][e] = 0.f;
   }
 }
 
@@ -405,7 +414,7 @@ __device__ __forceinline__ void kv2_phase(Kv2Ctx &x, int g, const Kv2Ids &ids, c
   } else if (n >= 1 && n - 1 < x.nq) {
     const int m = n - 1;
     kv2_accumulate(a, prev, (m & 3) == 3, x.slots + (m % kKv2Slots) * kKv2SlotBytes,
-                   x.xch + ((m & 1) * 4 + x.wave) * kKv2XBytes, NB, scale, dk_pool, dv_pool, x.wave, x.lane);
+                   x.xch + (m & 1) * 4 * kKv2XBytes, NB, scale, dk_pool, dv_pool, x.wave, x.lane);
   }
   kv2_barrier();
 }
@@ -508,8 +517,8 @@ bwd_kv2_kernel(uint16_t *__restrict__ dS, const uint16_t *__restrict__ Q, const 
     const int m = x.nq - 1;
     Kv2Ids last;
     kv2_ids(last, desc + (((m >> 2)) & 3) * kKv2Desc, x.lane);
-    kv2_accumulate(a, last, true, slots + (m % kKv2Slots) * kKv2SlotBytes,
-                   xch + ((m & 1) * 4 + x.wave) * kKv2XBytes, NB, scale, dk_pool, dv_pool, x.wave, x.lane);
+    kv2_accumulate(a, last, true, slots + (m % kKv2Slots) * kKv2SlotBytes, xch + (m & 1) * 4 * kKv2XBytes, NB,
+                   scale, dk_pool, dv_pool, x.wave, x.lane);
   }
 #undef KV2_PHASES
 }
