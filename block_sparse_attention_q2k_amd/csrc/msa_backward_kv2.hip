@@ -28,8 +28,8 @@
 // occupy the matrix unit.  One barrier per phase.  The Q / dO rows of each quarter are
 // gathered by the accumulate waves (its LSE and delta by the first of them), kKv2Ahead
 // quarters ahead, into a ring of kKv2Slots LDS slots, staged through registers for two
-// phases; each task row's ids are read two rows ahead, by the first accumulate wave, into
-// a ring of descriptors.  With two waves per SIMD the compiler keeps every accumulator in
+// phases; each task row's ids are read two rows ahead, by the second accumulate wave,
+// into a ring of descriptors.  With two waves per SIMD the compiler keeps every accumulator in
 // ordinary VGPRs.
 #include "msa_walk.h"  // uniform()
 
@@ -382,7 +382,10 @@ struct Kv2Ctx {
 // ids: the score waves' row g; for the accumulate waves, the row whose quarters they
 // gather in this row's phases (g + 1, or the last row) and prev: row g - 1 (its last
 // quarter is accumulated in phase 4 g).
-template <int QTR, bool SCORE, bool LEAD>
+// ROLE of an accumulate wave besides its products and gather (a template argument, so
+// that no wave's code has a conditional load): 1 moves LSE and delta (the first wave), 2
+// the task-row descriptors (the second), 0 nothing more.
+template <int QTR, bool SCORE, int ROLE>
 __device__ __forceinline__ void kv2_phase(Kv2Ctx &x, int g, const Kv2Ids &ids, const Kv2Ids &prev,
                                           const Kv2Ids &gat, Kv2Stage (&stg)[2], int &dstg, Kv2Score &s,
                                           Kv2Acc &a,
@@ -397,13 +400,13 @@ __device__ __forceinline__ void kv2_phase(Kv2Ctx &x, int g, const Kv2Ids &ids, c
   const int n = 4 * g + QTR;
   if constexpr (!SCORE) {
     if (n >= 2) kv2_gather_store(x.slots + ((n + 2) % kKv2Slots) * kKv2SlotBytes, stg[QTR & 1], x.tid - 256);
-    if (LEAD && QTR == 2 && x.lane < kKv2Desc)
+    if (ROLE == 2 && QTR == 2 && x.lane < kKv2Desc)
       x.desc[((g + 2) & 3) * kKv2Desc + x.lane] = kv2_desc_pad(dstg, x.lane, ds_spare);
     // quarter n + kKv2Ahead = quarter QTR of row g + 1 (gat); past the end, a valid
     // quarter (unused)
     const int qa = g + 1 < x.R.total ? QTR : 3;
-    kv2_gather_load<LEAD>(stg[QTR & 1], gat.i, gat.t[2 * qa], gat.t[2 * qa + 1], Q, dO, LSE, Delta, x.tid - 256);
-    if (LEAD && QTR == 0) dstg = kv2_desc_load(x.R, g + 2, meta, qrows, qpos, qtile, x.lane);
+    kv2_gather_load<ROLE == 1>(stg[QTR & 1], gat.i, gat.t[2 * qa], gat.t[2 * qa + 1], Q, dO, LSE, Delta, x.tid - 256);
+    if (ROLE == 2 && QTR == 0) dstg = kv2_desc_load(x.R, g + 2, meta, qrows, qpos, qtile, x.lane);
   }
   if constexpr (SCORE) {
     if (n < x.nq)
@@ -499,7 +502,7 @@ bwd_kv2_kernel(uint16_t *__restrict__ dS, const uint16_t *__restrict__ Q, const 
     s.bucket = -1;
     s.kbase = 0;
     kv2_score_ops(s, slots, x.lane);  // quarter 0
-    KV2_PHASES(true, false)
+    KV2_PHASES(true, 0)
   } else {
     Kv2Stage stg[2];
     Kv2Score s;  // unused
@@ -509,9 +512,11 @@ bwd_kv2_kernel(uint16_t *__restrict__ dS, const uint16_t *__restrict__ Q, const 
 #pragma unroll
       for (int e = 0; e < 16; ++e) a.dk[nd][e] = a.dv[nd][e] = 0.f;
     if (x.wave == 0) {
-      KV2_PHASES(false, true)
+      KV2_PHASES(false, 1)
+    } else if (x.wave == 1) {
+      KV2_PHASES(false, 2)
     } else {
-      KV2_PHASES(false, false)
+      KV2_PHASES(false, 0)
     }
     // the last quarter (phase nq)
     const int m = x.nq - 1;
