@@ -156,8 +156,8 @@ TRAFFIC_SOURCES = ["msa_abi.hip", "msa_backward.hip", "msa_backward_kv.hip", "ms
                    "msa_backward_dqs.hip", "msa_index.hip", "msa_walk.h", "msa_device.h", "msa_launch.h",
                    "../build.py"]
 TRAFFIC_RECORD = {"config": 2, "dq_mode": "stored",
-                  "sha256": "ecd5cc849c15c5863509b0eee41dd2a7613f6e97ebb01e28779122bbdbce4bb9",
-                  "bytes": 17029742599}  # read 12.511 GB + written 4.518 GB
+                  "sha256": "e0c9d4856d1491f7badffd5c69896df3beb208dbd57cf3a3ca8aafeb35c5aaac",
+                  "bytes": 17031003473}  # read 12.513 GB + written 4.518 GB
 
 
 def sources_digest():
