@@ -317,7 +317,7 @@ struct KvState {
   f32x16 dkacc[4], dvacc[4];
   bf16x8 kf[8], vf[8];
   int cur_r, kbase, gb;
-  int r_row, nv_row;  // bucket and valid-query count of the row about to be computed
+  int r_row;  // bucket of the row about to be computed
   float lse2, del;
   int pos;
   int idv;      // ids of the next row (kv_ids_load)
@@ -390,9 +390,8 @@ __device__ __forceinline__ void kv_row(
   const int tid = kv_opaque(tid_in);
   const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
   const int j16 = lane & 15, G = l32 >> 4;
-  const lds_char *lcur = (const lds_char *)cur;
   // this row's meta entry came with the previous row's ids (no scalar load to wait for)
-  const int r = st.r_row, nv = st.nv_row;
+  const int r = st.r_row;
   // 1. new bucket: this wave's K/V slices (issued before the asynchronous gather so that
   //    waiting for them never waits for the gather)
   if (r != st.cur_r) {
@@ -462,7 +461,6 @@ __device__ __forceinline__ void kv_row(
   // 5. scalars of row + 1 -> LDS; everyone done with `cur` and done writing `nxt`
   if (more && tid < 128) kv_store_scalars(nxt_sc, tid, st.lse2, st.del, st.pos);
   st.r_row = r_next;
-  st.nv_row = __builtin_amdgcn_readlane(st.idv, 17);
   st.idv = idv2;
   kv_lds_barrier();
 }
@@ -490,7 +488,6 @@ bwd_kv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kw,
       KvRowIds ids;
       const i32x4 m0 = meta[lo];
       st.r_row = m0[0];
-      st.nv_row = m0[1];
       kv_row_ids(ids, qrows, qpos, lo, m0[1]);
       st.idv = lo + 1 < hi ? kv_ids_load(qrows, qpos, meta, lo + 1, tid & 63) : 0;
       if (tid < 128) {

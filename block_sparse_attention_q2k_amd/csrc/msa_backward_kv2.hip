@@ -223,7 +223,7 @@ __device__ __forceinline__ void kv2_score(Kv2Score &s, const Kv2Ids &D, int qtr,
                                           const char *sl_next, char *xs,
                                           uint16_t *__restrict__ dS, const uint16_t *__restrict__ Kw,
                                           const uint16_t *__restrict__ Vw, const int32_t *__restrict__ cu_ws,
-                                          int ndocs, int NB, float c, int ds_spare, int wave, int lane) {
+                                          int ndocs, int NB, float c, int wave, int lane) {
   const int l32 = lane & 31, h = lane >> 5;
   const int bucket = D.bucket;
   if (bucket != s.bucket) {  // new bucket: this wave's K / V rows
@@ -412,8 +412,7 @@ __device__ __forceinline__ void kv2_phase(Kv2Ctx &x, int g, const Kv2Ids &ids, c
     if (n < x.nq)
       kv2_score(s, ids, QTR, x.slots + (n % kKv2Slots) * kKv2SlotBytes,
                 x.slots + ((n + 1) % kKv2Slots) * kKv2SlotBytes,
-                x.xch + ((n & 1) * 4 + x.wave) * kKv2XBytes, dS, Kw, Vw, cu_ws, ndocs, NB, c, ds_spare, x.wave,
-                x.lane);
+                x.xch + ((n & 1) * 4 + x.wave) * kKv2XBytes, dS, Kw, Vw, cu_ws, ndocs, NB, c, x.wave, x.lane);
   } else if (n >= 1 && n - 1 < x.nq) {
     const int m = n - 1;
     kv2_accumulate(a, prev, (m & 3) == 3, x.slots + (m % kKv2Slots) * kKv2SlotBytes,
