@@ -156,8 +156,8 @@ TRAFFIC_SOURCES = ["msa_abi.hip", "msa_backward.hip", "msa_backward_kv.hip", "ms
                    "msa_backward_dqs.hip", "msa_index.hip", "msa_walk.h", "msa_device.h", "msa_launch.h",
                    "../build.py"]
 TRAFFIC_RECORD = {"config": 2, "dq_mode": "stored",
-                  "sha256": "e7143da5fd4c8f02556ee62ea8d2c8b747eb37900d353cd82a8ff3c1a99ee1d7",
-                  "bytes": 17036911752}  # read 12.519 GB + written 4.518 GB
+                  "sha256": "0a084c40d23aed043dc0609c269f6976ffcf2d803cca3ecf3f4bf10618dce840",
+                  "bytes": 17028221665}  # read 12.510 GB + written 4.518 GB
 
 
 def sources_digest():

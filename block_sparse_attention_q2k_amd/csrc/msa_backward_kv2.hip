@@ -27,10 +27,10 @@
 // waves of a SIMD the score wave's softmax issues while the accumulate wave's products
 // occupy the matrix unit.  One barrier per phase.  The Q / dO rows of each quarter are
 // gathered by the accumulate waves (its LSE and delta by the first of them), kKv2Ahead
-// quarters ahead, into a ring of kKv2Slots LDS slots, staged through registers for two
-// phases; each task row's ids are read two rows ahead, by the second accumulate wave,
-// into a ring of descriptors.  With two waves per SIMD the compiler keeps every accumulator in
-// ordinary VGPRs.
+// quarters ahead, into a ring of kKv2Slots LDS slots, with asynchronous global-to-LDS
+// copies that no register holds; each task row's ids are copied two rows ahead, by the
+// second accumulate wave, and completed into a ring of descriptors.  With two waves per
+// SIMD the compiler keeps every accumulator in ordinary VGPRs.
 #include "msa_walk.h"  // uniform()
 
 namespace msa {
@@ -42,11 +42,11 @@ constexpr int kKv2Half = 8192;               // Q rows of a quarter: 32 x 256 B;
 constexpr int kKv2SlotBytes = 2 * kKv2Half + 256;  // + LSE (log2) and delta of the 32 rows
 constexpr int kKv2XBytes = 4096;             // P, dS of one wave's keys for one quarter
 constexpr int kKv2Desc = 32;                 // words per task-row descriptor
-// The gather of quarter n + kKv2Ahead, loaded in phase n and stored in phase n + 2, goes
-// to the slot of quarter n + kKv2Ahead - kKv2Slots, which the accumulate waves last read
-// in phase n + kKv2Ahead - kKv2Slots + 1; it must be done by then, and stored before the
-// score waves read it in phase n + kKv2Ahead.
-static_assert(kKv2Ahead - kKv2Slots + 1 < 2 && kKv2Ahead >= 3, "gather ring");
+// The copies of quarter n + kKv2Ahead, issued in phase n, go to the slot of quarter n +
+// kKv2Ahead - kKv2Slots, which the accumulate waves last read in phase n + kKv2Ahead -
+// kKv2Slots + 1 (before phase n); they must land before the score waves read the
+// quarter's A operands in phase n + kKv2Ahead - 1.
+static_assert(kKv2Ahead - kKv2Slots + 1 < 0 && kKv2Ahead >= 3, "gather ring");
 
 // Descriptor words: 0 index head, 1 bucket, 2 valid queries, 3 the bucket of the
 // workgroup's next row (-1 past the last), 4..11 query ids, 12..19 positions, 20..27
@@ -94,10 +94,14 @@ __device__ __forceinline__ void kv2_row(const Kv2Rows &R, int g, int &i, int &ro
   }
 }
 
-// Descriptor word `lane` (< 32) of the workgroup's row g (clamped to its last row).
-__device__ __forceinline__ int kv2_desc_load(const Kv2Rows &R, int g, const i32x4 *__restrict__ meta,
-                                             const int32_t *__restrict__ qrows, const int32_t *__restrict__ qpos,
-                                             const int32_t *__restrict__ qtile, int lane) {
+// Descriptor word `lane` (< 32; lanes 32-63 repeat lanes 24-31's sources) of the
+// workgroup's row g (clamped to its last row): the address it is loaded from
+// (kv2_desc_src; words 0 and 3 not yet final) and the completed word (kv2_desc_fix), so
+// that a wave can copy the words ahead and complete them where it uses them.
+__device__ __forceinline__ const int32_t *kv2_desc_src(const Kv2Rows &R, int g, const i32x4 *__restrict__ meta,
+                                                       const int32_t *__restrict__ qrows,
+                                                       const int32_t *__restrict__ qpos,
+                                                       const int32_t *__restrict__ qtile, int lane) {
   g = min(g, R.total - 1);
   int i, row;
   kv2_row(R, g, i, row);
@@ -107,8 +111,18 @@ __device__ __forceinline__ int kv2_desc_load(const Kv2Rows &R, int g, const i32x
                        : lane < kDescPos  ? qrows + (size_t)row * kTileQ + (lane - kDescT)
                        : lane < kDescTile ? qpos + (size_t)row * kTileQ + (lane - kDescPos)
                        : qtile + (size_t)row * kTileQ + ((lane - kDescTile) & 7);
-  const int v = *src;
+  return src;
+}
+__device__ __forceinline__ int kv2_desc_fix(int v, const Kv2Rows &R, int g, int lane) {
+  g = min(g, R.total - 1);
+  int i, row;
+  kv2_row(R, g, i, row);
   return lane == kDescI ? i : lane == kDescNext ? (g + 1 < R.total ? v : -1) : v;
+}
+__device__ __forceinline__ int kv2_desc_load(const Kv2Rows &R, int g, const i32x4 *__restrict__ meta,
+                                             const int32_t *__restrict__ qrows, const int32_t *__restrict__ qpos,
+                                             const int32_t *__restrict__ qtile, int lane) {
+  return kv2_desc_fix(*kv2_desc_src(R, g, meta, qrows, qpos, qtile, lane), R, g, lane);
 }
 
 // The padding rule applied to descriptor word v of lane `lane` (every lane of the wave
@@ -122,49 +136,62 @@ __device__ __forceinline__ int kv2_desc_pad(int v, int lane, int ds_spare) {
   return v;
 }
 
-// Gather of one quarter (registers), by the 256 threads of the accumulate waves (at =
-// thread index among them): chunks at and at + 256 of the quarter's Q rows and of its
-// dO rows (chunk ci: row rq = ci / 16 of the quarter, query 2 q + rq / 16, head rq % 16;
-// physical chunk ci % 16, which holds logical chunk (ci % 16) ^ f(rq)) and, for at < 16,
-// 4 rows of LSE (at < 8) or delta (rows 4 m .. 4 m + 3, m = at % 8: query m / 4, heads
-// 4 (m % 4) ..).
-struct Kv2Stage {
-  u32x4 q[2], o[2];
-  f32x4 s;
-};
-// LEAD: the first accumulate wave, which also moves LSE and delta (a template argument,
-// so that each wave's code has no conditional load and its memory waits stay exact).
+// Gather of one quarter into its LDS slot by the 256 threads of the accumulate waves
+// (at = thread index among them), as asynchronous global-to-LDS copies of 16 bytes per
+// lane (lane l of a wave lands at the wave's destination + 16 l): chunks at and at + 256
+// of the quarter's Q rows and of its dO rows (chunk ci: row rq = ci / 16 of the quarter,
+// query 2 q + rq / 16, head rq % 16; physical chunk ci % 16, which holds logical chunk
+// (ci % 16) ^ f(rq)) and, in the first accumulate wave (LEAD), 4 rows of LSE (lanes 0-7)
+// or delta (lanes 8-15) (rows 4 m .. 4 m + 3, m = at % 8: query m / 4, heads 4 (m % 4)
+// ..).  LSE lands in natural log; kv2_lse_log2 rescales it.  The copies count in the
+// issuing wave's vector-memory counter, which the wave waits on before the barrier that
+// publishes the slot.
+typedef __attribute__((address_space(1))) void kv2_gvoid;
+typedef __attribute__((address_space(3))) void kv2_lvoid;
+__device__ __forceinline__ void kv2_copy16(const void *src, char *dst) {
+  __builtin_amdgcn_global_load_lds((const kv2_gvoid *)src, (kv2_lvoid *)dst, 16, 0, 0);
+}
 template <bool LEAD>
-__device__ __forceinline__ void kv2_gather_load(Kv2Stage &st, int i, int t0, int t1, const uint16_t *__restrict__ Q,
-                                                const uint16_t *__restrict__ dO, const float *__restrict__ LSE,
-                                                const float *__restrict__ Delta, int at) {
+__device__ __forceinline__ void kv2_gather(char *slot, int i, int t0, int t1, const uint16_t *__restrict__ Q,
+                                           const uint16_t *__restrict__ dO, const float *__restrict__ LSE,
+                                           const float *__restrict__ Delta, int at) {
   // chunks at and at + 256 share the head (rq % 16) and the chunk, so one lane offset
   // serves both; the row base is wave-uniform
   const int hh = (at >> 4) & 15;
   const unsigned off = (unsigned)(hh * kD + (((at & 15) ^ kv2_f(hh)) << 3)) * 2u;  // bytes
+  char *dst = slot + uniform(at & ~63) * 16;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int t = j ? t1 : t0;  // rows 0..15: query 2 q, 16..31: query 2 q + 1
     const size_t base = ((size_t)t * kH + kHPI * i) * kD;
-    st.q[j] = *(const u32x4 *)((const char *)(Q + base) + off);
-    st.o[j] = *(const u32x4 *)((const char *)(dO + base) + off);
+    kv2_copy16((const char *)(Q + base) + off, dst + 256 * 16 * j);
+    kv2_copy16((const char *)(dO + base) + off, dst + kKv2Half + 256 * 16 * j);
   }
-  if constexpr (LEAD) {  // lanes 0..15 are used
-    const int m = at & 7;
-    const int ts = (m >> 2) ? t1 : t0;
-    const float *sb = (at & 8) ? Delta : LSE;
-    st.s = *(const f32x4 *)(sb + (size_t)ts * kH + kHPI * i + 4 * (m & 3));
+  if constexpr (LEAD) {
+    if (at < 16) {
+      const int m = at & 7;
+      const int ts = (m >> 2) ? t1 : t0;
+      const float *sb = (at & 8) ? Delta : LSE;
+      kv2_copy16(sb + (size_t)ts * kH + kHPI * i + 4 * (m & 3), slot + 2 * kKv2Half);
+    }
   }
 }
-__device__ __forceinline__ void kv2_gather_store(char *slot, const Kv2Stage &st, int at) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    *(u32x4 *)(slot + (at + 256 * j) * 16) = st.q[j];
-    *(u32x4 *)(slot + kKv2Half + (at + 256 * j) * 16) = st.o[j];
-  }
-  if (at < 16) {
-    const f32x4 v = (at & 8) ? st.s : st.s * kLog2e;
-    *(f32x4 *)(slot + 2 * kKv2Half + at * 16) = v;
+
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t kv2_lds_addr(const char *p) { return (uint32_t)(size_t)(const lds_char *)p; }
+
+// LSE of the quarter in slot sl from natural log to log2 (lanes 0-7 of the first
+// accumulate wave; its own copies, already waited for).  The compiler orders every LDS
+// access of the slot array behind all copies in flight; written as assembly (the read
+// waits within its statement), these accesses do not wait for the quarters gathered
+// ahead.
+__device__ __forceinline__ void kv2_lse_log2(char *sl, int lane) {
+  if (lane < 8) {
+    const uint32_t a = kv2_lds_addr(sl + 2 * kKv2Half) + 16 * lane;
+    f32x4 v;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+    v = v * kLog2e;
+    asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
   }
 }
 
@@ -314,28 +341,51 @@ __device__ __forceinline__ void kv2_accumulate(Kv2Acc &a, const Kv2Ids &D, bool 
                                                const char *xs0, int NB, float scale, float *__restrict__ dk_pool,
                                                float *__restrict__ dv_pool, int wave, int lane) {
   const int l32 = lane & 31, h = lane >> 5, j16 = lane & 15, G = l32 >> 4;
-  const lds_char *lq = (const lds_char *)sl;
   // B operands of k-step ks: lane (l32, h) gets dims 32 w + l32 of rows 16 ks + 8 hi +
   // 4 h + 0..3 (hi = 0, 1), matching the row order of the P / dS registers
+  // (rows 16 + r: 4096 bytes on; dO: kKv2Half on), read as assembly with the A operands of
+  // the first iteration (kv2_lse_log2 gives the reason), waiting within the statement
   bf16x8 ob[2], qb[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
+  bf16x8 pa[2], sa[2];
+  {
+    static_assert(kKv2Half == 8192, "immediate offsets");
     const int c0 = 32 * wave + 16 * G + 4 * (j16 & 3);
-    const uint32_t r0 = kv2_swz(16 * ks + 4 * h + (j16 >> 2), c0 * 2);
-    const uint32_t r1 = kv2_swz(16 * ks + 4 * h + (j16 >> 2) + 8, c0 * 2);
-    ob[ks] = cat8(lds_read_tr(lq, kKv2Half + r0), lds_read_tr(lq, kKv2Half + r1));
-    qb[ks] = cat8(lds_read_tr(lq, r0), lds_read_tr(lq, r1));
+    const uint32_t a0 = kv2_lds_addr(sl) + kv2_swz(4 * h + (j16 >> 2), c0 * 2);
+    const uint32_t a1 = kv2_lds_addr(sl) + kv2_swz(4 * h + (j16 >> 2) + 8, c0 * 2);
+    const uint32_t ax = kv2_lds_addr(xs0) + 16 * lane;
+    u32x2 q00, q01, q10, q11, o00, o01, o10, o11;
+    u32x4 p0, s0;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %10\n\t"
+        "ds_read_b64_tr_b16 %1, %11\n\t"
+        "ds_read_b64_tr_b16 %2, %10 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %3, %11 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %4, %10 offset:8192\n\t"
+        "ds_read_b64_tr_b16 %5, %11 offset:8192\n\t"
+        "ds_read_b64_tr_b16 %6, %10 offset:12288\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:12288\n\t"
+        "ds_read_b128 %8, %12\n\t"
+        "ds_read_b128 %9, %12 offset:2048\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(q00), "=&v"(q01), "=&v"(q10), "=&v"(q11), "=&v"(o00), "=&v"(o01), "=&v"(o10), "=&v"(o11),
+          "=&v"(p0), "=&v"(s0)
+        : "v"(a0), "v"(a1), "v"(ax)
+        : "memory");
+    qb[0] = __builtin_bit_cast(bf16x8, u32x4{q00[0], q00[1], q01[0], q01[1]});
+    qb[1] = __builtin_bit_cast(bf16x8, u32x4{q10[0], q10[1], q11[0], q11[1]});
+    ob[0] = __builtin_bit_cast(bf16x8, u32x4{o00[0], o00[1], o01[0], o01[1]});
+    ob[1] = __builtin_bit_cast(bf16x8, u32x4{o10[0], o10[1], o11[0], o11[1]});
+    pa[0] = __builtin_bit_cast(bf16x8, p0);
+    sa[0] = __builtin_bit_cast(bf16x8, s0);
   }
   // Iteration it = (ks, kt) = (it / 4, it % 4); the A operands of iteration it + 1 are
   // read before the MFMAs of iteration it.
-  bf16x8 pa[2], sa[2];
   auto rd = [&](int it, int b) {
     const int ks = it >> 2, kt = it & 3;
     const char *xs = xs0 + kt * kKv2XBytes;
     pa[b] = *(const bf16x8 *)(xs + ((0 + ks) * 64 + lane) * 16);
     sa[b] = *(const bf16x8 *)(xs + ((2 + ks) * 64 + lane) * 16);
   };
-  rd(0, 0);
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     if (it + 1 < 8) rd(it + 1, (it + 1) & 1);
@@ -366,13 +416,14 @@ __device__ __forceinline__ void kv2_accumulate(Kv2Acc &a, const Kv2Ids &D, bool 
   }
 }
 
-// One phase n = 4 g + QTR: store the gather of quarter n + 2 (loaded in phase n - 2),
-// load the gather of quarter n + kKv2Ahead, move the descriptor of row g + 2 (loaded in
-// phase 4 g, stored in phase 4 g + 2), the score waves' quarter n (if n < nq) and the
-// accumulate waves' quarter n - 1 (if n >= 1), then the barrier.
+// One phase n = 4 g + QTR: move the descriptor of row g + 2 (copied in phase 4 g,
+// completed and stored in phase 4 g + 3), issue the copies of quarter n + kKv2Ahead, rescale the LSE of
+// quarter n + 1, the score waves' quarter n (if n < nq) and the accumulate waves' quarter
+// n - 1 (if n >= 1); the accumulate waves then wait for their copies of quarter n + 2
+// (issued in phase n - 2), and the barrier.
 struct Kv2Ctx {
   char *slots, *xch;
-  int *desc;
+  int *desc, *dstage;
   Kv2Rows R;
   int nq;
   bool score;
@@ -387,7 +438,7 @@ struct Kv2Ctx {
 // the task-row descriptors (the second), 0 nothing more.
 template <int QTR, bool SCORE, int ROLE>
 __device__ __forceinline__ void kv2_phase(Kv2Ctx &x, int g, const Kv2Ids &ids, const Kv2Ids &prev,
-                                          const Kv2Ids &gat, Kv2Stage (&stg)[2], int &dstg, Kv2Score &s,
+                                          const Kv2Ids &gat, Kv2Score &s,
                                           Kv2Acc &a,
                                           const uint16_t *__restrict__ Q, const uint16_t *__restrict__ dO,
                                           const float *__restrict__ LSE, const float *__restrict__ Delta,
@@ -398,15 +449,30 @@ __device__ __forceinline__ void kv2_phase(Kv2Ctx &x, int g, const Kv2Ids &ids, c
                                           int ndocs, int NB, float c, float scale, float *__restrict__ dk_pool,
                                           float *__restrict__ dv_pool, int ds_spare) {
   const int n = 4 * g + QTR;
+  static_assert(kKv2Ahead == 4 && kKv2Slots == 6, "copy schedule");
   if constexpr (!SCORE) {
-    if (n >= 2) kv2_gather_store(x.slots + ((n + 2) % kKv2Slots) * kKv2SlotBytes, stg[QTR & 1], x.tid - 256);
-    if (ROLE == 2 && QTR == 2 && x.lane < kKv2Desc)
-      x.desc[((g + 2) & 3) * kKv2Desc + x.lane] = kv2_desc_pad(dstg, x.lane, ds_spare);
+    if (ROLE == 2 && QTR == 0)  // the words of row g + 2, copied to the staging area
+      __builtin_amdgcn_global_load_lds((const kv2_gvoid *)kv2_desc_src(x.R, g + 2, meta, qrows, qpos, qtile, x.lane),
+                                       (kv2_lvoid *)x.dstage, 4, 0, 0);
+    if (ROLE == 2 && QTR == 3) {
+      // the staged words (their copy, issued before phase 4 g's gather, was waited for at
+      // the end of phase 4 g + 2) completed into the descriptor ring; read and stored as
+      // assembly, which the compiler does not order behind the copies in flight
+      int v;
+      const uint32_t a = kv2_lds_addr((const char *)x.dstage) + 4 * (x.lane & 31);
+      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+      v = kv2_desc_pad(kv2_desc_fix(v, x.R, g + 2, x.lane), x.lane, ds_spare);
+      if (x.lane < kKv2Desc) {
+        const uint32_t d = kv2_lds_addr((const char *)(x.desc + ((g + 2) & 3) * kKv2Desc)) + 4 * x.lane;
+        asm volatile("ds_write_b32 %0, %1" ::"v"(d), "v"(v) : "memory");
+      }
+    }
     // quarter n + kKv2Ahead = quarter QTR of row g + 1 (gat); past the end, a valid
     // quarter (unused)
     const int qa = g + 1 < x.R.total ? QTR : 3;
-    kv2_gather_load<ROLE == 1>(stg[QTR & 1], gat.i, gat.t[2 * qa], gat.t[2 * qa + 1], Q, dO, LSE, Delta, x.tid - 256);
-    if (ROLE == 2 && QTR == 0) dstg = kv2_desc_load(x.R, g + 2, meta, qrows, qpos, qtile, x.lane);
+    kv2_gather<ROLE == 1>(x.slots + ((n + kKv2Ahead) % kKv2Slots) * kKv2SlotBytes, gat.i, gat.t[2 * qa],
+                          gat.t[2 * qa + 1], Q, dO, LSE, Delta, x.tid - 256);
+    if (ROLE == 1) kv2_lse_log2(x.slots + ((n + 1) % kKv2Slots) * kKv2SlotBytes, x.lane);
   }
   if constexpr (SCORE) {
     if (n < x.nq)
@@ -417,6 +483,14 @@ __device__ __forceinline__ void kv2_phase(Kv2Ctx &x, int g, const Kv2Ids &ids, c
     const int m = n - 1;
     kv2_accumulate(a, prev, (m & 3) == 3, x.slots + (m % kKv2Slots) * kKv2SlotBytes,
                    x.xch + (m & 1) * 4 * kKv2XBytes, NB, scale, dk_pool, dv_pool, x.wave, x.lane);
+  }
+  if constexpr (!SCORE) {
+    // this wave's loads issued after the copies of phase n - 2, which complete in order:
+    // its copies of phases n - 1 and n (4 each, 5 in the first wave) and, in the second,
+    // the descriptor copy issued first in phase 4 g (the dK / dV atomics of a flush, which
+    // may complete out of order, only make the wait longer)
+    constexpr int kAfter = ROLE == 1 ? 10 : (ROLE == 2 && QTR <= 1) ? 9 : 8;
+    WAIT_VMCNT(kAfter);
   }
   kv2_barrier();
 }
@@ -432,11 +506,13 @@ bwd_kv2_kernel(uint16_t *__restrict__ dS, const uint16_t *__restrict__ Q, const 
   __shared__ __attribute__((aligned(16))) char slots[kKv2Slots * kKv2SlotBytes];
   __shared__ __attribute__((aligned(16))) char xch[2 * 4 * kKv2XBytes];
   __shared__ int desc[4 * kKv2Desc];
+  __shared__ int dstage[64];
   const int c = blockIdx.x, tid = threadIdx.x;
   Kv2Ctx x;
   x.slots = slots;
   x.xch = xch;
   x.desc = desc;
+  x.dstage = dstage;
   x.tid = tid;
   x.lane = tid & 63;
   x.wave = uniform((tid >> 6) & 3);
@@ -467,15 +543,14 @@ bwd_kv2_kernel(uint16_t *__restrict__ dS, const uint16_t *__restrict__ Q, const 
     kv2_ids(d0, desc, x.lane);
     if (!x.score) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        Kv2Stage t;
-        kv2_gather_load<true>(t, d0.i, d0.t[2 * q], d0.t[2 * q + 1], Q, dO, LSE, Delta, tid - 256);
-        kv2_gather_store(slots + q * kKv2SlotBytes, t, tid - 256);
-      }
+      for (int q = 0; q < 4; ++q)
+        kv2_gather<true>(slots + q * kKv2SlotBytes, d0.i, d0.t[2 * q], d0.t[2 * q + 1], Q, dO, LSE, Delta, tid - 256);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the copies of quarters 0-3
   __syncthreads();
-  int dstg = 0;
+  if (tid >= 256 && tid < 264) kv2_lse_log2(slots, tid - 256);  // quarter 0 (1-3: phases 0-2)
+  __syncthreads();
 #define KV2_PHASES(SC, LD)                                                                                      \
   for (int g = 0; g < x.R.total; ++g) {                                                                     \
     Kv2Ids ids, prev, gat;                                                                                  \
@@ -484,18 +559,17 @@ bwd_kv2_kernel(uint16_t *__restrict__ dS, const uint16_t *__restrict__ Q, const 
       kv2_ids(ids, desc + (g & 3) * kKv2Desc, x.lane);                                                      \
     else                                                                                                    \
       kv2_ids(prev, desc + ((g + 3) & 3) * kKv2Desc, x.lane);                                               \
-    kv2_phase<0, SC, LD>(x, g, ids, prev, gat, stg, dstg, s, a, Q, dO, LSE, Delta, dS, Kw, Vw, meta, qrows, qpos, qtile, cu_ws, \
+    kv2_phase<0, SC, LD>(x, g, ids, prev, gat, s, a, Q, dO, LSE, Delta, dS, Kw, Vw, meta, qrows, qpos, qtile, cu_ws, \
                      ndocs, NB, scale_log2e, scale, dk_pool, dv_pool, ds_spare);                           \
-    kv2_phase<1, SC, LD>(x, g, ids, prev, gat, stg, dstg, s, a, Q, dO, LSE, Delta, dS, Kw, Vw, meta, qrows, qpos, qtile, cu_ws, \
+    kv2_phase<1, SC, LD>(x, g, ids, prev, gat, s, a, Q, dO, LSE, Delta, dS, Kw, Vw, meta, qrows, qpos, qtile, cu_ws, \
                      ndocs, NB, scale_log2e, scale, dk_pool, dv_pool, ds_spare);                           \
-    kv2_phase<2, SC, LD>(x, g, ids, prev, gat, stg, dstg, s, a, Q, dO, LSE, Delta, dS, Kw, Vw, meta, qrows, qpos, qtile, cu_ws, \
+    kv2_phase<2, SC, LD>(x, g, ids, prev, gat, s, a, Q, dO, LSE, Delta, dS, Kw, Vw, meta, qrows, qpos, qtile, cu_ws, \
                      ndocs, NB, scale_log2e, scale, dk_pool, dv_pool, ds_spare);                           \
-    kv2_phase<3, SC, LD>(x, g, ids, prev, gat, stg, dstg, s, a, Q, dO, LSE, Delta, dS, Kw, Vw, meta, qrows, qpos, qtile, cu_ws, \
+    kv2_phase<3, SC, LD>(x, g, ids, prev, gat, s, a, Q, dO, LSE, Delta, dS, Kw, Vw, meta, qrows, qpos, qtile, cu_ws, \
                      ndocs, NB, scale_log2e, scale, dk_pool, dv_pool, ds_spare);                           \
   }
   // each role runs its own loop, so that only its own state is live in it
   if (x.score) {
-    Kv2Stage stg[2];  // unused
     Kv2Score s;
     Kv2Acc a;  // unused
     s.bucket = -1;
@@ -503,7 +577,6 @@ bwd_kv2_kernel(uint16_t *__restrict__ dS, const uint16_t *__restrict__ Q, const 
     kv2_score_ops(s, slots, x.lane);  // quarter 0
     KV2_PHASES(true, 0)
   } else {
-    Kv2Stage stg[2];
     Kv2Score s;  // unused
     Kv2Acc a;
 #pragma unroll
@@ -523,6 +596,8 @@ bwd_kv2_kernel(uint16_t *__restrict__ dS, const uint16_t *__restrict__ Q, const 
     kv2_ids(last, desc + (((m >> 2)) & 3) * kKv2Desc, x.lane);
     kv2_accumulate(a, last, true, slots + (m % kKv2Slots) * kKv2SlotBytes, xch + (m & 1) * 4 * kKv2XBytes, NB,
                    scale, dk_pool, dv_pool, x.wave, x.lane);
+    // the copies issued ahead of the end must land before the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 #undef KV2_PHASES
 }
