@@ -156,8 +156,8 @@ TRAFFIC_SOURCES = ["msa_abi.hip", "msa_backward.hip", "msa_backward_kv.hip", "ms
                    "msa_backward_dqs.hip", "msa_index.hip", "msa_walk.h", "msa_device.h", "msa_launch.h",
                    "../build.py"]
 TRAFFIC_RECORD = {"config": 2, "dq_mode": "stored",
-                  "sha256": "0a084c40d23aed043dc0609c269f6976ffcf2d803cca3ecf3f4bf10618dce840",
-                  "bytes": 17028221665}  # read 12.510 GB + written 4.518 GB
+                  "sha256": "f6a36f1a09f7b06235e0d2c840e65380a5e38f217482ea17c7d0ad6a8ee6015a",
+                  "bytes": 17034090629}  # read 12.516 GB + written 4.518 GB
 
 
 def sources_digest():

@@ -386,6 +386,12 @@ __device__ __forceinline__ void kv2_accumulate(Kv2Acc &a, const Kv2Ids &D, bool 
     pa[b] = *(const bf16x8 *)(xs + ((0 + ks) * 64 + lane) * 16);
     sa[b] = *(const bf16x8 *)(xs + ((2 + ks) * 64 + lane) * 16);
   };
+  // the products run at raised wave priority, so that the SIMD's matrix unit takes them
+  // ahead of the score wave's while both are ready (1-1.5 % faster; the score wave's
+  // products first, the other way round, was 8 % slower)
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(2);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     if (it + 1 < 8) rd(it + 1, (it + 1) & 1);
@@ -394,6 +400,8 @@ __device__ __forceinline__ void kv2_accumulate(Kv2Acc &a, const Kv2Ids &D, bool 
     a.dk[kt] = mfma32(sa[it & 1], qb[ks], a.dk[kt]);
     __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
   if (last_qtr && D.next != D.bucket) {
     const int i = D.i;
     const int gb = D.bucket - i * NB;
